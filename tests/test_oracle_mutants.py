@@ -1,0 +1,99 @@
+"""Plants one plausible mistake at a time in a copy of the C oracle, builds the
+copy, and checks that the pins in test_oracle_pins.py reject it.  This shows
+the pins are tied to the pages and to mathematics rather than to the oracle's
+own code.  Everything here runs on the CPU."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "mrr_oracle.c")
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("rank order reversed",
+     "float a = (float)load_value(in[0], i, tin);",
+     "float a = (float)load_value(in[nranks - 1], i, tin);"),
+    ("rank order: peers reversed",
+     "float x = (float)load_value(in[r], i, tin);",
+     "float x = (float)load_value(in[nranks - r], i, tin);"),
+    ("accumulator starts at +0",
+     "float a = (float)load_value(in[0], i, tin);",
+     "float a = 0.0f + (float)load_value(in[0], i, tin);"),
+    ("last rank dropped",
+     "for (int r = 1; r < nranks; ++r) {",
+     "for (int r = 1; r < nranks - 1; ++r) {"),
+    ("native accumulation not rounded",
+     "for (int r = 1; r < nranks; ++r) a = round_to(acc, a + load_value(in[r], i, tin));",
+     "for (int r = 1; r < nranks; ++r) a = a + load_value(in[r], i, tin);\n  a = round_to(acc, a);"),
+    ("fp8 bias 14", "else v = ldexp(1.0 + (double)m / 8.0, e - 15);",
+     "else v = ldexp(1.0 + (double)m / 8.0, e - 14);"),
+    ("fp8 subnormal scale", "else if (e == 0) v = ldexp((double)m / 8.0, -14);",
+     "else if (e == 0) v = ldexp((double)m / 8.0, -15);"),
+    ("fp8 saturation lost",
+     "if (a >= fp8_tab[FP8_NFIN - 1]) return s | (uint8_t)(FP8_NFIN - 1);",
+     "if (a >= fp8_tab[FP8_NFIN - 1]) return s | (uint8_t)0x78;"),
+    ("f16 subnormal scale", "else if (e == 0) v = ldexp((double)m, -24);",
+     "else if (e == 0) v = ldexp((double)m, -25);"),
+    ("f16 bias 16", "else v = ldexp(1.0 + (double)m / 1024.0, e - 15);",
+     "else v = ldexp(1.0 + (double)m / 1024.0, e - 16);"),
+    ("ties away from zero", "return (lo % 2 == 0) ? lo : hi;", "return hi;"),
+    ("ties toward zero", "return (lo % 2 == 0) ? lo : hi;", "return lo;"),
+    ("bf16 overflow threshold", "bf16_tab[BF16_NFIN] = ldexp(1.0, 128);",
+     "bf16_tab[BF16_NFIN] = ldexp(1.0, 129);"),
+    ("packet flag in the low word", "return ((uint64_t)flag << 32) | (uint64_t)word;",
+     "return ((uint64_t)word << 32) | (uint64_t)flag;"),
+    ("packet tail not zero-padded", "uint32_t byte = at < nbytes ? src[at] : 0;",
+     "uint32_t byte = at < nbytes ? src[at] : 0xFF;"),
+    ("scratch indexed [src][dst]", "((size_t)d * nranks + s) * npkt;",
+     "((size_t)s * nranks + d) * npkt;"),
+]
+
+
+def _checks():
+    """The pins, bound to fixed parameters, cheapest first."""
+    return [
+        pins.test_fp8_format_facts_from_pages,
+        pins.test_fp8_decode_matches_fp16_route,
+        pins.test_fp8_worked_values,
+        pins.test_fp8_encode_ties_and_saturation,
+        pins.test_fp8_encode_all_f16_inputs_brute_force,
+        pins.test_f16_decode_all_codes,
+        pins.test_bf16_decode_all_codes,
+        pins.test_f16_narrow_from_f64_vs_numpy,
+        pins.test_bf16_narrow_from_f32_vs_torch,
+        pins.test_rank_order_pin_f32,
+        pins.test_signed_zero_and_cancellation,
+        lambda o: pins.test_constant_buffers_sum_to_n_times_c(o, 8, "f16", 0.5),
+        lambda o: pins.test_constant_fp8_buffers(o, 32),
+        lambda o: pins.test_f32_sum_vs_numpy_sequential(o, 8),
+        lambda o: pins.test_f16_sum_vs_numpy(o, 4),
+        lambda o: pins.test_fp8_native_and_f16_accumulation(o),
+        pins.test_pack_layout_worked_example,
+        pins.test_pack_unpack_roundtrip,
+        lambda o: pins.test_allreduce_packet_expectation(o, "f16", 1001),
+    ]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_planted_mistake(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site for %r not unique" % name
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.build(force=True, src=str(mutant_src), out=str(tmp_path / "mutant.so"))
+    orc = oracle.load(lib)
+    for check in _checks():
+        try:
+            check(orc)
+        except (AssertionError, ValueError):
+            return  # a pin caught it
+    pytest.fail("no pin rejected the planted mistake: %s" % name)
+
+
+def test_unmutated_oracle_passes_every_check(orc):
+    for check in _checks():
+        check(orc)
