@@ -1,0 +1,191 @@
+"""Python binding of libmrr, the MI355X N-rank allreduce reduction library.
+
+Argument marshalling only: every function forwards to the C entry point of the
+same name in ``libmrr.so`` (declared in ``include/mrr.h``) and returns its
+``mrr_status`` as an int.  Buffers may be torch tensors (their ``data_ptr()``
+is passed) or raw device addresses (ints).  ``stream=None`` means torch's
+current HIP stream on the current device.
+
+The library must have been built (``__graft_entry__.build()`` or
+``python allreduce_reduction_nranks_amd/build.py``); without it every call
+raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmrr.so")
+
+# mrr_status
+MRR_OK, MRR_EINVAL, MRR_EUNSUPPORTED, MRR_EALIGN, MRR_EOVERLAP, MRR_ESCRATCH, \
+    MRR_ETIMEDOUT, MRR_EHIP = range(8)
+STATUS_NAMES = ["MRR_OK", "MRR_EINVAL", "MRR_EUNSUPPORTED", "MRR_EALIGN", "MRR_EOVERLAP",
+                "MRR_ESCRATCH", "MRR_ETIMEDOUT", "MRR_EHIP"]
+# mrr_dtype
+MRR_AUTO, MRR_F32, MRR_F16, MRR_BF16, MRR_FP8_E4M3B15 = range(5)
+DTYPES = {"auto": MRR_AUTO, "f32": MRR_F32, "f16": MRR_F16, "bf16": MRR_BF16,
+          "fp8": MRR_FP8_E4M3B15, "fp8_e4m3b15": MRR_FP8_E4M3B15}
+MAX_RANKS = 32
+PKT_FLAG_SLOTS = 1024
+
+
+class MrrError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__("%s%s" % (name, (": " + what) if what else ""))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads libmrr.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmrr.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32
+        pp = ctypes.POINTER(vp)
+        sigs = {
+            "mrr_allreduce_rsag": ([pp, pp, sz, i, i, vp], i),
+            "mrr_allreduce_rsag_ex": ([pp, pp, sz, i, i, i, i, i, vp], i),
+            "mrr_packet_scratch_bytes": ([sz, i, i], sz),
+            "mrr_packet_flag_bytes": ([i], sz),
+            "mrr_allreduce_packet": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, vp], i),
+            "mrr_allreduce_packet_ex": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, i, i, vp], i),
+            "mrr_packet_reduce": ([pp, vp, sz, i, i, i, u32, u32, u32, vp, vp], i),
+            "mrr_pack": ([vp, vp, sz, u32, vp], i),
+            "mrr_unpack": ([vp, vp, sz, vp], i),
+            "mrr_fp8b15_to_f16": ([vp, vp, sz, vp], i),
+            "mrr_fp8b15_to_f32": ([vp, vp, sz, vp], i),
+            "mrr_f16_to_fp8b15": ([vp, vp, sz, vp], i),
+            "mrr_f32_to_fp8b15": ([vp, vp, sz, vp], i),
+            "mrr_status_string": ([i], ctypes.c_char_p),
+            "mrr_version": ([], i),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+        return _lib
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _ptrs(xs):
+    return (ctypes.c_void_p * len(xs))(*[_ptr(x) for x in xs])
+
+
+def _dt(d) -> int:
+    if isinstance(d, int):
+        return d
+    if isinstance(d, str):
+        return DTYPES[d]
+    import torch
+    return {torch.float32: MRR_F32, torch.float16: MRR_F16, torch.bfloat16: MRR_BF16,
+            torch.uint8: MRR_FP8_E4M3B15}[d]
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def check(status: int, what: str = "") -> None:
+    """Raises MrrError for a non-OK status."""
+    if status != MRR_OK:
+        raise MrrError(status, what)
+
+
+def mrr_status_string(status: int) -> str:
+    return load_library().mrr_status_string(status).decode()
+
+
+def mrr_version() -> int:
+    return load_library().mrr_version()
+
+
+def mrr_allreduce_rsag(inputs, outputs, count, dtype, nranks, stream=None) -> int:
+    return load_library().mrr_allreduce_rsag(_ptrs(inputs), _ptrs(outputs), count, _dt(dtype),
+                                             nranks, _stream(stream))
+
+
+def mrr_allreduce_rsag_ex(inputs, outputs, count, dtype_in, accum, dtype_out, nranks, rank=-1,
+                          stream=None) -> int:
+    return load_library().mrr_allreduce_rsag_ex(_ptrs(inputs), _ptrs(outputs), count,
+                                                _dt(dtype_in), _dt(accum), _dt(dtype_out),
+                                                nranks, rank, _stream(stream))
+
+
+def mrr_packet_scratch_bytes(count, dtype, nranks) -> int:
+    return load_library().mrr_packet_scratch_bytes(count, _dt(dtype), nranks)
+
+
+def mrr_packet_flag_bytes(nranks) -> int:
+    return load_library().mrr_packet_flag_bytes(nranks)
+
+
+def mrr_allreduce_packet(inputs, outputs, scratch, scratch_bytes, flags, count, dtype, accum,
+                         nranks, max_spins, dev_err=None, stream=None) -> int:
+    return load_library().mrr_allreduce_packet(
+        _ptrs(inputs), _ptrs(outputs), _ptr(scratch), scratch_bytes, _ptr(flags), count,
+        _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), _stream(stream))
+
+
+def mrr_allreduce_packet_ex(inputs, outputs, scratch, scratch_bytes, flags, count, dtype, accum,
+                            nranks, max_spins, dev_err=None, blocks_per_rank=0, threads=0,
+                            stream=None) -> int:
+    return load_library().mrr_allreduce_packet_ex(
+        _ptrs(inputs), _ptrs(outputs), _ptr(scratch), scratch_bytes, _ptr(flags), count,
+        _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), blocks_per_rank, threads,
+        _stream(stream))
+
+
+def mrr_packet_reduce(in_pkts, out_pkts, npkts, dtype, accum, nranks, flag_in, flag_out,
+                      max_spins, dev_err=None, stream=None) -> int:
+    return load_library().mrr_packet_reduce(_ptrs(in_pkts), _ptr(out_pkts), npkts, _dt(dtype),
+                                            _dt(accum), nranks, flag_in, flag_out, max_spins,
+                                            _ptr(dev_err), _stream(stream))
+
+
+def mrr_pack(src, pkts, nbytes, flag, stream=None) -> int:
+    return load_library().mrr_pack(_ptr(src), _ptr(pkts), nbytes, flag, _stream(stream))
+
+
+def mrr_unpack(pkts, dst, nbytes, stream=None) -> int:
+    return load_library().mrr_unpack(_ptr(pkts), _ptr(dst), nbytes, _stream(stream))
+
+
+def mrr_fp8b15_to_f16(src, dst, n, stream=None) -> int:
+    return load_library().mrr_fp8b15_to_f16(_ptr(src), _ptr(dst), n, _stream(stream))
+
+
+def mrr_fp8b15_to_f32(src, dst, n, stream=None) -> int:
+    return load_library().mrr_fp8b15_to_f32(_ptr(src), _ptr(dst), n, _stream(stream))
+
+
+def mrr_f16_to_fp8b15(src, dst, n, stream=None) -> int:
+    return load_library().mrr_f16_to_fp8b15(_ptr(src), _ptr(dst), n, _stream(stream))
+
+
+def mrr_f32_to_fp8b15(src, dst, n, stream=None) -> int:
+    return load_library().mrr_f32_to_fp8b15(_ptr(src), _ptr(dst), n, _stream(stream))

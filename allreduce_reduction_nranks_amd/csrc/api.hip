@@ -1,0 +1,329 @@
+// api.hip -- the libmrr C ABI: argument validation, type resolution and
+// dispatch to the kernel launchers.  Every check that needs no device runs
+// before any HIP call, so a refused call never touches the GPU.
+#include <mutex>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "mrr_device.hpp"
+#include "mrr_internal.hpp"
+
+namespace mrr {
+
+static bool log_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("MRR_LOG");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+static mrr_status refuse(mrr_status st, const char* fn, const char* why) {
+  if (log_enabled()) fprintf(stderr, "libmrr: %s refused (%s): %s\n", fn, mrr_status_string(st), why);
+  return st;
+}
+
+static int tsize(int t) {
+  switch (t) {
+    case kF32: return 4;
+    case kF16: return 2;
+    case kBF16: return 2;
+    case kFP8: return 1;
+    default: return 0;
+  }
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+static bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// outputs[k] may be exactly inputs[k] (same start and length); any other
+// overlap of an output with any input or output is refused.
+static bool bad_overlap(const void* const* in, size_t in_bytes, void* const* out, size_t out_bytes,
+                        int n) {
+  for (int k = 0; k < n; ++k) {
+    const Range o{(uintptr_t)out[k], (uintptr_t)out[k] + out_bytes};
+    for (int r = 0; r < n; ++r) {
+      const Range i{(uintptr_t)in[r], (uintptr_t)in[r] + in_bytes};
+      if (!overlaps(o, i)) continue;
+      if (r == k && o.lo == i.lo && out_bytes == in_bytes) continue;
+      return true;
+    }
+    for (int j = k + 1; j < n; ++j) {
+      const Range q{(uintptr_t)out[j], (uintptr_t)out[j] + out_bytes};
+      if (overlaps(o, q)) return true;
+    }
+  }
+  return false;
+}
+
+static bool valid_nranks(int n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32; }
+
+static mrr_status hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return MRR_OK;
+  if (log_enabled()) fprintf(stderr, "libmrr: %s: HIP error %s\n", fn, hipGetErrorString(e));
+  return MRR_EHIP;
+}
+
+int device_cu_count(int device) {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  if (device < 0 && hipGetDevice(&device) != hipSuccess) return 0;
+  if (device < 0 || device >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[device] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+      return 0;
+    cached[device] = cus;
+  }
+  return cached[device];
+}
+
+// Workgroups of `kernel` at `threads` threads that fit on the device at once.
+static int max_resident_blocks(const void* kernel, int threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return 0;
+  return per_cu * device_cu_count(dev);
+}
+
+}  // namespace mrr
+
+using namespace mrr;
+
+extern "C" {
+
+const char* mrr_status_string(mrr_status s) {
+  switch (s) {
+    case MRR_OK: return "MRR_OK: success";
+    case MRR_EINVAL: return "MRR_EINVAL: invalid argument";
+    case MRR_EUNSUPPORTED: return "MRR_EUNSUPPORTED: rank count or type combination not supported";
+    case MRR_EALIGN: return "MRR_EALIGN: pointer misaligned";
+    case MRR_EOVERLAP: return "MRR_EOVERLAP: output overlaps another buffer";
+    case MRR_ESCRATCH: return "MRR_ESCRATCH: packet scratch too small";
+    case MRR_ETIMEDOUT: return "MRR_ETIMEDOUT: packet poll exceeded max_spins";
+    case MRR_EHIP: return "MRR_EHIP: HIP runtime error";
+  }
+  return "unknown mrr_status";
+}
+
+int mrr_version(void) { return 10000; }
+
+mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs, size_t count,
+                                 mrr_dtype in, mrr_dtype accum, mrr_dtype out, int nranks,
+                                 int rank, void* stream) {
+  static const char* fn = "mrr_allreduce_rsag";
+  if (!valid_nranks(nranks)) return refuse(MRR_EUNSUPPORTED, fn, "nranks not in {2,4,8,16,32}");
+  if (rank < -1 || rank >= nranks) return refuse(MRR_EINVAL, fn, "rank outside [-1, nranks)");
+  if (!inputs || !outputs) return refuse(MRR_EINVAL, fn, "null pointer array");
+  const int tin = (int)in;
+  const int tacc = accum == MRR_AUTO ? tin : (int)accum;
+  const int tout = out == MRR_AUTO ? tin : (int)out;
+  if (!tsize(tin) || !rsag_supported(nranks, tin, tacc, tout))
+    return refuse(MRR_EUNSUPPORTED, fn, "type combination");
+  if (count == 0) return MRR_OK;
+  const size_t ein = tsize(tin), eout = tsize(tout);
+  if (count > (SIZE_MAX / 4) / eout) return refuse(MRR_EINVAL, fn, "count too large");
+  bool vec = true;
+  for (int r = 0; r < nranks; ++r) {
+    if (!inputs[r] || !outputs[r]) return refuse(MRR_EINVAL, fn, "null buffer");
+    if (!aligned(inputs[r], ein) || !aligned(outputs[r], eout))
+      return refuse(MRR_EALIGN, fn, "buffer not aligned to its element size");
+    vec = vec && aligned(inputs[r], 16) && aligned(outputs[r], 16);
+  }
+  if (bad_overlap(inputs, count * ein, outputs, count * eout, nranks))
+    return refuse(MRR_EOVERLAP, fn, "output overlaps another buffer");
+  RsagPlan plan{nranks, tin, tacc, tout, count, rank, vec};
+  return hip_status(launch_rsag(plan, inputs, outputs, (hipStream_t)stream), fn);
+}
+
+mrr_status mrr_allreduce_rsag(const void* const* inputs, void* const* outputs, size_t count,
+                              mrr_dtype dtype, int nranks, void* stream) {
+  return mrr_allreduce_rsag_ex(inputs, outputs, count, dtype, MRR_F32, MRR_AUTO, nranks, -1,
+                               stream);
+}
+
+size_t mrr_packet_scratch_bytes(size_t count, mrr_dtype dtype, int nranks) {
+  const int e = tsize((int)dtype);
+  if (!e || nranks <= 0) return 0;
+  const size_t npkt = (count * (size_t)e + 3) / 4;
+  return (size_t)nranks * (size_t)nranks * npkt * 8;
+}
+
+size_t mrr_packet_flag_bytes(int nranks) {
+  return nranks <= 0 ? 0 : (size_t)nranks * MRR_PKT_FLAG_SLOTS * sizeof(uint32_t);
+}
+
+mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outputs, void* scratch,
+                                   size_t scratch_bytes, uint32_t* flags, size_t count,
+                                   mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                   uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
+                                   int threads, void* stream) {
+  static const char* fn = "mrr_allreduce_packet";
+  if (!valid_nranks(nranks)) return refuse(MRR_EUNSUPPORTED, fn, "nranks not in {2,4,8,16,32}");
+  if (!inputs || !outputs || !scratch || !flags)
+    return refuse(MRR_EINVAL, fn, "null pointer argument");
+  const int t = (int)dtype;
+  const int tacc = accum == MRR_AUTO ? t : (int)accum;
+  if (!tsize(t) || !packet_supported(nranks, t, tacc))
+    return refuse(MRR_EUNSUPPORTED, fn, "type combination");
+  if (threads != 0 && (threads < 64 || threads > 1024 || threads % 64 != 0))
+    return refuse(MRR_EINVAL, fn, "threads must be a multiple of 64 in [64, 1024]");
+  if (blocks_per_rank < 0 || blocks_per_rank > MRR_PKT_FLAG_SLOTS)
+    return refuse(MRR_EINVAL, fn, "blocks_per_rank outside [1, MRR_PKT_FLAG_SLOTS]");
+  if (!aligned(scratch, 8) || !aligned(flags, 4)) return refuse(MRR_EALIGN, fn, "scratch/flags");
+  if (count == 0) return MRR_OK;
+  const size_t e = tsize(t);
+  if (count > (SIZE_MAX / 64) / e) return refuse(MRR_EINVAL, fn, "count too large");
+  for (int r = 0; r < nranks; ++r) {
+    if (!inputs[r] || !outputs[r]) return refuse(MRR_EINVAL, fn, "null buffer");
+    if (!aligned(inputs[r], 4) || !aligned(outputs[r], 4))
+      return refuse(MRR_EALIGN, fn, "buffers must be 4-byte aligned");
+  }
+  const size_t nbytes = count * e;
+  if (bad_overlap(inputs, nbytes, outputs, nbytes, nranks))
+    return refuse(MRR_EOVERLAP, fn, "output overlaps another buffer");
+  const size_t need = mrr_packet_scratch_bytes(count, dtype, nranks);
+  if (scratch_bytes < need) return refuse(MRR_ESCRATCH, fn, "scratch smaller than required");
+  const Range sr{(uintptr_t)scratch, (uintptr_t)scratch + need};
+  const Range fr{(uintptr_t)flags, (uintptr_t)flags + mrr_packet_flag_bytes(nranks)};
+  if (overlaps(sr, fr)) return refuse(MRR_EOVERLAP, fn, "scratch overlaps flags");
+  for (int r = 0; r < nranks; ++r) {
+    const Range ir{(uintptr_t)inputs[r], (uintptr_t)inputs[r] + nbytes};
+    const Range orr{(uintptr_t)outputs[r], (uintptr_t)outputs[r] + nbytes};
+    if (overlaps(sr, ir) || overlaps(sr, orr) || overlaps(fr, ir) || overlaps(fr, orr))
+      return refuse(MRR_EOVERLAP, fn, "scratch/flags overlap a data buffer");
+  }
+
+  const uint64_t npkt = (nbytes + 3) / 4;
+  const int T = threads ? threads : 512;
+  int B = blocks_per_rank;
+  // Geometry needs the device: how many workgroups fit at once.
+  const void* kernel = packet_allpair_kernel(nranks, t, tacc);
+  const int resident = max_resident_blocks(kernel, T);
+  if (resident <= 0) return hip_status(hipErrorInvalidDevice, fn);
+  const int max_b = resident / nranks;
+  if (B == 0) {
+    // About 4 packets per lane, as many blocks as fit, never more than slots.
+    const uint64_t want = (npkt + (uint64_t)T * 4 - 1) / ((uint64_t)T * 4);
+    B = (int)(want < 1 ? 1 : want);
+    if (B > max_b) B = max_b;
+    if (B > MRR_PKT_FLAG_SLOTS) B = MRR_PKT_FLAG_SLOTS;
+  }
+  if (B < 1 || B > max_b)
+    return refuse(MRR_EINVAL, fn, "nranks * blocks_per_rank workgroups do not fit on the GPU at once");
+
+  PacketArgs a = {};
+  for (int r = 0; r < nranks; ++r) {
+    a.in[r] = inputs[r];
+    a.out[r] = outputs[r];
+  }
+  a.scratch = (uint64_t*)scratch;
+  a.flags = flags;
+  a.dev_err = dev_err;
+  a.nbytes = nbytes;
+  a.npkt = npkt;
+  a.pkts_per_block = (npkt + (uint64_t)B - 1) / (uint64_t)B;
+  a.nblocks = (uint32_t)B;
+  a.max_spins = max_spins;
+  return hip_status(launch_packet_allpair(a, nranks, t, tacc, T, (hipStream_t)stream), fn);
+}
+
+mrr_status mrr_allreduce_packet(const void* const* inputs, void* const* outputs, void* scratch,
+                                size_t scratch_bytes, uint32_t* flags, size_t count,
+                                mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                uint32_t max_spins, uint32_t* dev_err, void* stream) {
+  return mrr_allreduce_packet_ex(inputs, outputs, scratch, scratch_bytes, flags, count, dtype,
+                                 accum, nranks, max_spins, dev_err, 0, 0, stream);
+}
+
+mrr_status mrr_packet_reduce(const uint64_t* const* in_pkts, uint64_t* out_pkts, size_t npkts,
+                             mrr_dtype dtype, mrr_dtype accum, int nranks, uint32_t flag_in,
+                             uint32_t flag_out, uint32_t max_spins, uint32_t* dev_err,
+                             void* stream) {
+  static const char* fn = "mrr_packet_reduce";
+  if (!valid_nranks(nranks)) return refuse(MRR_EUNSUPPORTED, fn, "nranks not in {2,4,8,16,32}");
+  if (!in_pkts || !out_pkts) return refuse(MRR_EINVAL, fn, "null pointer argument");
+  const int t = (int)dtype;
+  const int tacc = accum == MRR_AUTO ? t : (int)accum;
+  if (!tsize(t) || !packet_supported(nranks, t, tacc))
+    return refuse(MRR_EUNSUPPORTED, fn, "type combination");
+  if (npkts == 0) return MRR_OK;
+  if (npkts > SIZE_MAX / 64) return refuse(MRR_EINVAL, fn, "npkts too large");
+  if (!aligned(out_pkts, 8)) return refuse(MRR_EALIGN, fn, "out_pkts");
+  const Range o{(uintptr_t)out_pkts, (uintptr_t)out_pkts + npkts * 8};
+  PacketReduceArgs a = {};
+  for (int r = 0; r < nranks; ++r) {
+    if (!in_pkts[r]) return refuse(MRR_EINVAL, fn, "null packet buffer");
+    if (!aligned(in_pkts[r], 8)) return refuse(MRR_EALIGN, fn, "in_pkts");
+    const Range i{(uintptr_t)in_pkts[r], (uintptr_t)in_pkts[r] + npkts * 8};
+    if (overlaps(o, i)) return refuse(MRR_EOVERLAP, fn, "out_pkts overlaps an input");
+    a.in[r] = in_pkts[r];
+  }
+  a.out = out_pkts;
+  a.dev_err = dev_err;
+  a.npkts = npkts;
+  a.flag_in = flag_in;
+  a.flag_out = flag_out;
+  a.max_spins = max_spins;
+  return hip_status(launch_packet_reduce(a, nranks, t, tacc, (hipStream_t)stream), fn);
+}
+
+mrr_status mrr_pack(const void* src, uint64_t* pkts, size_t nbytes, uint32_t flag, void* stream) {
+  static const char* fn = "mrr_pack";
+  if (nbytes == 0) return MRR_OK;
+  if (!src || !pkts) return refuse(MRR_EINVAL, fn, "null pointer");
+  if (nbytes > SIZE_MAX / 4) return refuse(MRR_EINVAL, fn, "nbytes too large");
+  if (!aligned(src, 4) || !aligned(pkts, 8)) return refuse(MRR_EALIGN, fn, "src 4 / pkts 8 bytes");
+  const Range s{(uintptr_t)src, (uintptr_t)src + nbytes};
+  const Range p{(uintptr_t)pkts, (uintptr_t)pkts + (nbytes + 3) / 4 * 8};
+  if (overlaps(s, p)) return refuse(MRR_EOVERLAP, fn, "src overlaps pkts");
+  return hip_status(launch_pack(src, pkts, nbytes, flag, (hipStream_t)stream), fn);
+}
+
+mrr_status mrr_unpack(const uint64_t* pkts, void* dst, size_t nbytes, void* stream) {
+  static const char* fn = "mrr_unpack";
+  if (nbytes == 0) return MRR_OK;
+  if (!dst || !pkts) return refuse(MRR_EINVAL, fn, "null pointer");
+  if (nbytes > SIZE_MAX / 4) return refuse(MRR_EINVAL, fn, "nbytes too large");
+  if (!aligned(dst, 4) || !aligned(pkts, 8)) return refuse(MRR_EALIGN, fn, "dst 4 / pkts 8 bytes");
+  const Range d{(uintptr_t)dst, (uintptr_t)dst + nbytes};
+  const Range p{(uintptr_t)pkts, (uintptr_t)pkts + (nbytes + 3) / 4 * 8};
+  if (overlaps(d, p)) return refuse(MRR_EOVERLAP, fn, "dst overlaps pkts");
+  return hip_status(launch_unpack(pkts, dst, nbytes, (hipStream_t)stream), fn);
+}
+
+static mrr_status codec(int dir, const void* in, size_t ein, void* out, size_t eout, size_t n,
+                        void* stream, const char* fn) {
+  if (n == 0) return MRR_OK;
+  if (!in || !out) return refuse(MRR_EINVAL, fn, "null pointer");
+  if (n > (SIZE_MAX / 8)) return refuse(MRR_EINVAL, fn, "n too large");
+  if (!aligned(in, ein) || !aligned(out, eout)) return refuse(MRR_EALIGN, fn, "element alignment");
+  const Range i{(uintptr_t)in, (uintptr_t)in + n * ein};
+  const Range o{(uintptr_t)out, (uintptr_t)out + n * eout};
+  if (overlaps(i, o)) return refuse(MRR_EOVERLAP, fn, "in overlaps out");
+  const bool vec = aligned(in, 16) && aligned(out, 16);
+  return hip_status(launch_codec(dir, in, out, n, vec, (hipStream_t)stream), fn);
+}
+
+mrr_status mrr_fp8b15_to_f16(const uint8_t* in, uint16_t* out, size_t n, void* stream) {
+  return codec(0, in, 1, out, 2, n, stream, "mrr_fp8b15_to_f16");
+}
+mrr_status mrr_fp8b15_to_f32(const uint8_t* in, float* out, size_t n, void* stream) {
+  return codec(1, in, 1, out, 4, n, stream, "mrr_fp8b15_to_f32");
+}
+mrr_status mrr_f16_to_fp8b15(const uint16_t* in, uint8_t* out, size_t n, void* stream) {
+  return codec(2, in, 2, out, 1, n, stream, "mrr_f16_to_fp8b15");
+}
+mrr_status mrr_f32_to_fp8b15(const float* in, uint8_t* out, size_t n, void* stream) {
+  return codec(3, in, 4, out, 1, n, stream, "mrr_f32_to_fp8b15");
+}
+
+}  // extern "C"

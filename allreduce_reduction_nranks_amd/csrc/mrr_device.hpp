@@ -1,0 +1,231 @@
+// mrr_device.hpp -- element types, 16-byte vectors and conversions for gfx950.
+//
+// Type ids equal the public mrr_dtype values.  Every conversion here is exact
+// (widening) or a single round-to-nearest-even (narrowing); FP8 E4M3B15
+// narrowing saturates at +-0.9375.  The FP8 format (4 exponent bits, bias 15,
+// 3 mantissa bits, largest finite 0.9375) is the one defined in the MSCCL++
+// commit history entry adding the fp8_e4m3b15 datatype; since 0.9375 is the
+// largest finite value, exponent field 15 encodes inf (mantissa 0) and NaN.
+//
+// Kernels are compiled without fast-math and with f32/f16 denormals kept, so
+// f32 adds are IEEE binary32 adds and hardware converts honour denormals.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mrr {
+
+enum : int { kF32 = 1, kF16 = 2, kBF16 = 3, kFP8 = 4 };
+
+template <int T> struct Ty;
+template <> struct Ty<kF32> { static constexpr int size = 4; };
+template <> struct Ty<kF16> { static constexpr int size = 2; };
+template <> struct Ty<kBF16> { static constexpr int size = 2; };
+template <> struct Ty<kFP8> { static constexpr int size = 1; };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Memory access helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld_stream(const void* base, uint64_t vec) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + vec);
+}
+__device__ __forceinline__ void st_stream(void* base, uint64_t vec, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base) + vec);
+}
+// 64-bit packet access, coherent across the XCDs of one device.
+__device__ __forceinline__ uint64_t ld_pkt(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_pkt(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Scalar conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// FP8 E4M3B15 -> f32.  Moving the code's exponent and mantissa into the top of
+// an f32's fields gives 2^(e-127) * (1.m) (or the f32 denormal m * 2^-129 for
+// e = 0); multiplying by 2^112 rebiases to 2^(e-15) exactly.
+__device__ __forceinline__ float fp8_to_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 24;
+  float v = __uint_as_float((c & 0x7Fu) << 20) * 0x1p112f;
+  uint32_t u = __float_as_uint(v);
+  if ((c & 0x78u) == 0x78u) u = (c & 7u) ? 0x7FC00000u : 0x7F800000u;
+  return __uint_as_float(u | sign);
+}
+
+// FP8 E4M3B15 -> f16 bits: both formats have exponent bias 15, so the fields
+// line up after a shift.
+__device__ __forceinline__ uint32_t fp8_to_f16(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 8;
+  uint32_t mag = (c & 0x7Fu) << 7;
+  if ((c & 0x78u) == 0x78u) mag = (c & 7u) ? 0x7E00u : 0x7C00u;
+  return sign | mag;
+}
+
+// f32 -> FP8 E4M3B15, one round-to-nearest-even, saturating.
+//  |x| >= 2^-14: rebias the exponent by -112 in the bit pattern, then round
+//   the 23-bit mantissa to 3 bits by adding 2^19 - 1 plus the kept lsb; a
+//   carry rolls into the exponent.  Anything past 0x77 (including inf)
+//   clamps to 0x77.
+//  |x| <  2^-14: the subnormal step is 2^-17, so the code is rint(|x| * 2^17)
+//   (exact scaling, RNE), which reaches 8 = the first normal code.
+__device__ __forceinline__ uint32_t f32_to_fp8(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;
+  uint32_t q;
+  if (a >= 0x38800000u) {
+    const uint32_t r = a - (112u << 23);
+    q = (r + 0x7FFFFu + ((r >> 20) & 1u)) >> 20;
+    q = q < 0x77u ? q : 0x77u;
+  } else {
+    q = (uint32_t)__builtin_rintf(__uint_as_float(a) * 0x1p17f);
+  }
+  return sign | q;
+}
+
+// f16 bits -> FP8 E4M3B15: drop 7 mantissa bits with round-to-nearest-even
+// (the biases agree, f16 subnormals land on FP8 subnormals), then saturate.
+__device__ __forceinline__ uint32_t f16_to_fp8(uint32_t h) {
+  const uint32_t sign = (h >> 8) & 0x80u;
+  const uint32_t mag = h & 0x7FFFu;
+  if (mag > 0x7C00u) return sign | 0x7Fu;
+  uint32_t q = (mag + 0x3Fu + ((mag >> 7) & 1u)) >> 7;
+  q = q < 0x77u ? q : 0x77u;
+  return sign | q;
+}
+
+// ---------------------------------------------------------------------------
+// Generic element access by type id (T)
+// ---------------------------------------------------------------------------
+template <int T> __device__ __forceinline__ float to_f32(uint32_t bits);
+template <> __device__ __forceinline__ float to_f32<kF32>(uint32_t b) { return __uint_as_float(b); }
+template <> __device__ __forceinline__ float to_f32<kF16>(uint32_t b) { return f16_to_f32(b); }
+template <> __device__ __forceinline__ float to_f32<kBF16>(uint32_t b) { return bf16_to_f32(b); }
+template <> __device__ __forceinline__ float to_f32<kFP8>(uint32_t b) { return fp8_to_f32(b); }
+
+template <int T> __device__ __forceinline__ uint32_t from_f32(float f);
+template <> __device__ __forceinline__ uint32_t from_f32<kF32>(float f) { return __float_as_uint(f); }
+template <> __device__ __forceinline__ uint32_t from_f32<kF16>(float f) { return f32_to_f16(f); }
+template <> __device__ __forceinline__ uint32_t from_f32<kBF16>(float f) { return f32_to_bf16(f); }
+template <> __device__ __forceinline__ uint32_t from_f32<kFP8>(float f) { return f32_to_fp8(f); }
+
+// Rounds an f32 partial sum to the accumulator type.  The f32 add before it is
+// itself rounded, but f32 carries at least 2p+2 bits for p = 11 (f16), 8 (bf16)
+// and 4 (FP8), so the two roundings equal one correct rounding of the exact
+// sum.  FP8 sums of two FP8 values are exact in f32 in any case.
+template <int A> __device__ __forceinline__ float round_acc(float s);
+template <> __device__ __forceinline__ float round_acc<kF32>(float s) { return s; }
+template <> __device__ __forceinline__ float round_acc<kF16>(float s) { return (float)(_Float16)s; }
+template <> __device__ __forceinline__ float round_acc<kBF16>(float s) {
+  return bf16_to_f32(f32_to_bf16(s));
+}
+template <> __device__ __forceinline__ float round_acc<kFP8>(float s) {
+  return fp8_to_f32(f32_to_fp8(s));
+}
+
+// Element i of a buffer of type T, widened to f32.
+template <int T> __device__ __forceinline__ float load_elem(const void* p, uint64_t i) {
+  if constexpr (T == kF32) return __uint_as_float(reinterpret_cast<const uint32_t*>(p)[i]);
+  else if constexpr (Ty<T>::size == 2) return to_f32<T>(reinterpret_cast<const uint16_t*>(p)[i]);
+  else return to_f32<T>(reinterpret_cast<const uint8_t*>(p)[i]);
+}
+template <int T> __device__ __forceinline__ void store_elem(void* p, uint64_t i, float v) {
+  if constexpr (T == kF32) reinterpret_cast<uint32_t*>(p)[i] = __float_as_uint(v);
+  else if constexpr (Ty<T>::size == 2) reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)from_f32<T>(v);
+  else reinterpret_cast<uint8_t*>(p)[i] = (uint8_t)from_f32<T>(v);
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte vector decode / encode.  An input vector holds VW = 16 / size(In)
+// elements; its output holds VW * size(Out) bytes = OV 16-byte vectors.
+// ---------------------------------------------------------------------------
+template <int T> struct Vec {
+  static constexpr int VW = 16 / Ty<T>::size;
+};
+
+template <int T> __device__ __forceinline__ void decode16(const u32x4 v, float* x) {
+  if constexpr (T == kF32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(v[j]);
+  } else if constexpr (T == kF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // copy the lane out first: a bit_cast applied to a vector element
+      // expression reads element 0 whatever the index
+      const uint32_t w = v[j];
+      const f32x2 p = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+      x[2 * j] = p.x;
+      x[2 * j + 1] = p.y;
+    }
+  } else if constexpr (T == kBF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(v[j] << 16);
+      x[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) x[4 * j + b] = fp8_to_f32((v[j] >> (8 * b)) & 0xFFu);
+    }
+  }
+}
+
+// Packs n = 16 / size(T) f32 values (already members of T, or to be rounded
+// into T) into one 16-byte vector of type T.
+template <int T> __device__ __forceinline__ u32x4 encode16(const float* x) {
+  u32x4 v;
+  if constexpr (T == kF32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __float_as_uint(x[j]);
+  } else if constexpr (T == kF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x2 p;
+      p.x = x[2 * j];
+      p.y = x[2 * j + 1];
+      v[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
+    }
+  } else if constexpr (T == kBF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x2 p;
+      p.x = x[2 * j];
+      p.y = x[2 * j + 1];
+      v[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w |= f32_to_fp8(x[4 * j + b]) << (8 * b);
+      v[j] = w;
+    }
+  }
+  return v;
+}
+
+}  // namespace mrr

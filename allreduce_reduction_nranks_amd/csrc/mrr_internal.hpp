@@ -1,0 +1,92 @@
+// mrr_internal.hpp -- kernel argument blocks and launcher entry points shared
+// between the C-ABI layer (api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mrr.h"
+
+namespace mrr {
+
+constexpr int kMaxRanks = MRR_MAX_RANKS;
+constexpr int kFlagSlots = MRR_PKT_FLAG_SLOTS;
+
+// ---- RS/AG ----------------------------------------------------------------
+// Passed by value as the kernel argument block (< 4 KiB).
+struct RsagArgs {
+  const void* in[kMaxRanks];
+  void* out[kMaxRanks];
+  uint64_t chunk_vecs;    // chunk width C in 16-byte input vectors
+  uint64_t total_vecs;    // whole 16-byte input vectors in [0, count)
+  uint64_t tail_begin;    // first element not covered by a whole vector
+  uint32_t tail_count;    // elements in the tail handled by this launch (0..15)
+  uint32_t first_chunk;   // chunk handled by workgroup 0
+  uint32_t tiles_per_chunk;
+  uint32_t pad;
+};
+
+// Element-wise kernel arguments (pointers not 16-byte aligned).
+struct RsagScalarArgs {
+  const void* in[kMaxRanks];
+  void* out[kMaxRanks];
+  uint64_t begin, end;  // element range
+  int nranks;
+};
+
+struct RsagPlan {
+  int nranks;
+  int tin, tacc, tout;  // resolved type ids (no AUTO)
+  size_t count;
+  int rank;             // -1 = all chunks
+  bool vector;          // every pointer 16-byte aligned
+};
+
+hipError_t launch_rsag(const RsagPlan& plan, const void* const* inputs, void* const* outputs,
+                       hipStream_t stream);
+bool rsag_supported(int nranks, int tin, int tacc, int tout);
+
+// ---- LL packets -------------------------------------------------------------
+struct PacketArgs {
+  const void* in[kMaxRanks];
+  void* out[kMaxRanks];
+  uint64_t* scratch;       // [dst][src][npkt]
+  uint32_t* flags;         // [rank][kFlagSlots]
+  uint32_t* dev_err;       // may be null
+  uint64_t nbytes;         // payload bytes per rank
+  uint64_t npkt;           // packets per rank
+  uint64_t pkts_per_block; // slice width
+  uint32_t nblocks;        // B, blocks per rank
+  uint32_t max_spins;      // 0 = unbounded
+};
+
+struct PacketReduceArgs {
+  const uint64_t* in[kMaxRanks];
+  uint64_t* out;
+  uint32_t* dev_err;
+  uint64_t npkts;
+  uint32_t flag_in, flag_out;
+  uint32_t max_spins;
+};
+
+bool packet_supported(int nranks, int t, int tacc);
+// Pointer to the allpair kernel for (nranks, t, tacc), used for occupancy.
+const void* packet_allpair_kernel(int nranks, int t, int tacc);
+hipError_t launch_packet_allpair(const PacketArgs& a, int nranks, int t, int tacc, int threads,
+                                 hipStream_t stream);
+hipError_t launch_packet_reduce(const PacketReduceArgs& a, int nranks, int t, int tacc,
+                                hipStream_t stream);
+hipError_t launch_pack(const void* src, uint64_t* pkts, size_t nbytes, uint32_t flag,
+                       hipStream_t stream);
+hipError_t launch_unpack(const uint64_t* pkts, void* dst, size_t nbytes, hipStream_t stream);
+
+// ---- FP8 codec ----------------------------------------------------------------
+// dir: 0 fp8->f16, 1 fp8->f32, 2 f16->fp8, 3 f32->fp8
+hipError_t launch_codec(int dir, const void* in, void* out, size_t n, bool vector,
+                        hipStream_t stream);
+
+// ---- device properties ---------------------------------------------------------
+int device_cu_count(int device);
+
+}  // namespace mrr

@@ -1,0 +1,275 @@
+// packet.hip -- LL-packet (data + flag) allreduce kernels for gfx950.
+//
+// Protocol (MSCCL++ commit history for /src, entry fixing the
+// allreduce_allpair_packet algorithm; entry on the default flag buffer):
+// every rank sends its data as low-latency packets to every peer's scratch
+// area, never overwriting the input; the same workgroup sends, waits for its
+// peers' packets, reduces and writes back; the launch geometry is validated;
+// the flag update must cover every flag slot even when a workgroup has fewer
+// threads than slots; one flag buffer can be shared by calls of different
+// sizes and algorithms.
+//
+// A packet is 8 bytes: payload word k (bytes [4k, 4k+4) of the rank's
+// buffer, little-endian, zero past the end) in the low half, the call's flag
+// in the high half.  64-bit packet loads/stores are single-copy atomic, so a
+// reader that sees the flag also sees the payload written with it; they use
+// agent scope so the data is coherent across the 8 XCDs (each has its own
+// L2).  Readers poll a whole wavefront at a time and leave the loop together
+// once every lane's packets carry the flag (__all vote); the poll is bounded
+// by max_spins so a missing sender ends in an error word, not a hang.
+//
+// On one MI355X the N ranks are N groups of workgroups of one launch:
+// workgroup g is (rank d = g % N, block b = g / N).  Every workgroup waits
+// for its N-1 peers of the same slice, so the host checks that all N * B
+// workgroups fit on the GPU at once before launching.
+#include "mrr_device.hpp"
+#include "mrr_internal.hpp"
+
+namespace mrr {
+
+// Payload word k of a byte buffer of nbytes bytes (4-byte aligned).
+__device__ __forceinline__ uint32_t load_word(const void* src, uint64_t nbytes, uint64_t k) {
+  const uint64_t at = 4 * k;
+  if (at + 4 <= nbytes) return reinterpret_cast<const uint32_t*>(src)[k];
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(src);
+  uint32_t w = 0;
+  for (uint64_t i = at; i < nbytes; ++i) w |= (uint32_t)b[i] << (8 * (i - at));
+  return w;
+}
+
+// Writes the bytes of word k that lie inside [0, nbytes).
+__device__ __forceinline__ void store_word(void* dst, uint64_t nbytes, uint64_t k, uint32_t w) {
+  const uint64_t at = 4 * k;
+  if (at + 4 <= nbytes) {
+    reinterpret_cast<uint32_t*>(dst)[k] = w;
+    return;
+  }
+  uint8_t* b = reinterpret_cast<uint8_t*>(dst);
+  for (uint64_t i = at; i < nbytes; ++i) b[i] = (uint8_t)(w >> (8 * (i - at)));
+}
+
+__device__ __forceinline__ uint64_t make_pkt(uint32_t word, uint32_t flag) {
+  return ((uint64_t)flag << 32) | word;
+}
+
+// Element j of a payload word of type T, widened to f32.
+template <int T> __device__ __forceinline__ float word_elem(uint32_t w, int j) {
+  if constexpr (Ty<T>::size == 4) return __uint_as_float(w);
+  else if constexpr (Ty<T>::size == 2) return to_f32<T>((w >> (16 * j)) & 0xFFFFu);
+  else return to_f32<T>((w >> (8 * j)) & 0xFFu);
+}
+
+template <int T> __device__ __forceinline__ uint32_t elem_bits(float v) { return from_f32<T>(v); }
+
+// Reduces one payload word over N ranks in rank order; rank `self` (if < N)
+// contributes `own` instead of w[self].
+template <int N, int T, int Acc>
+__device__ __forceinline__ uint32_t reduce_word(const uint32_t* w, uint32_t self, uint32_t own) {
+  constexpr int E = 4 / Ty<T>::size;
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    float acc = round_acc<Acc>(word_elem<T>(self == 0u ? own : w[0], j));
+#pragma unroll
+    for (int s = 1; s < N; ++s)
+      acc = round_acc<Acc>(acc + word_elem<T>((uint32_t)s == self ? own : w[s], j));
+    out |= elem_bits<T>(acc) << (32 / E * j);
+  }
+  return out;
+}
+
+__device__ __forceinline__ void report_timeout(uint32_t* dev_err) {
+  if (dev_err) atomicCAS(dev_err, 0u, (uint32_t)MRR_ETIMEDOUT);
+}
+
+template <int N, int T, int Acc>
+__global__ void __launch_bounds__(1024) packet_allpair_k(const PacketArgs a) {
+  const uint32_t d = blockIdx.x % N;
+  const uint32_t b = blockIdx.x / N;
+  uint32_t* const my_flags = a.flags + (uint64_t)d * kFlagSlots;
+  uint32_t F = my_flags[b] + 1u;
+  if (F == 0u) F = 1u;
+
+  const uint64_t k_lo = (uint64_t)b * a.pkts_per_block;
+  const uint64_t k_hi = k_lo + a.pkts_per_block < a.npkt ? k_lo + a.pkts_per_block : a.npkt;
+  const void* src = a.in[d];
+
+  // Send: slice b of rank d's input, packed once, stored to every peer.
+  for (uint64_t k = k_lo + threadIdx.x; k < k_hi; k += blockDim.x) {
+    const uint64_t pkt = make_pkt(load_word(src, a.nbytes, k), F);
+#pragma unroll
+    for (int p = 0; p < N; ++p)
+      if ((uint32_t)p != d) st_pkt(a.scratch + ((uint64_t)p * N + d) * a.npkt + k, pkt);
+  }
+
+  // Receive, reduce and write back, a wavefront-uniform loop over the slice.
+  const uint64_t* const inbox = a.scratch + (uint64_t)d * N * a.npkt;
+  bool timed_out = false;
+  for (uint64_t kb = k_lo; kb < k_hi && !timed_out; kb += blockDim.x) {
+    const uint64_t k = kb + threadIdx.x;
+    const bool active = k < k_hi;
+    uint32_t w[N];
+    uint32_t pending = 0;
+#pragma unroll
+    for (int s = 0; s < N; ++s)
+      if (active && (uint32_t)s != d) pending |= 1u << s;
+    uint32_t spins = 0;
+    while (true) {
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        if (pending & (1u << s)) {
+          const uint64_t pk = ld_pkt(inbox + (uint64_t)s * a.npkt + k);
+          w[s] = (uint32_t)pk;
+          if ((uint32_t)(pk >> 32) == F) pending &= ~(1u << s);
+        }
+      }
+      if (__all(pending == 0u)) break;
+      if (a.max_spins != 0u && ++spins >= a.max_spins) {
+        report_timeout(a.dev_err);
+        timed_out = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (timed_out || !active) continue;
+    const uint32_t own = load_word(src, a.nbytes, k);
+    store_word(a.out[d], a.nbytes, k, reduce_word<N, T, Acc>(w, d, own));
+  }
+
+  // Flag update: every slot j of rank d with j % B == b, by a thread loop so
+  // that a workgroup with fewer threads than slots still covers them all.
+  __syncthreads();
+  for (uint32_t j = b + threadIdx.x * a.nblocks; j < (uint32_t)kFlagSlots;
+       j += blockDim.x * a.nblocks)
+    my_flags[j] = F;
+}
+
+// Receive step alone: packets from N producers outside the launch.
+template <int N, int T, int Acc>
+__global__ void __launch_bounds__(256) packet_reduce_k(const PacketReduceArgs a) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  bool timed_out = false;
+  for (uint64_t kb = (uint64_t)blockIdx.x * blockDim.x; kb < a.npkts && !timed_out; kb += stride) {
+    const uint64_t k = kb + threadIdx.x;
+    const bool active = k < a.npkts;
+    uint32_t w[N];
+    uint32_t pending = 0;
+#pragma unroll
+    for (int s = 0; s < N; ++s)
+      if (active) pending |= 1u << s;
+    uint32_t spins = 0;
+    while (true) {
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        if (pending & (1u << s)) {
+          const uint64_t pk = ld_pkt(a.in[s] + k);
+          w[s] = (uint32_t)pk;
+          if ((uint32_t)(pk >> 32) == a.flag_in) pending &= ~(1u << s);
+        }
+      }
+      if (__all(pending == 0u)) break;
+      if (a.max_spins != 0u && ++spins >= a.max_spins) {
+        report_timeout(a.dev_err);
+        timed_out = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (timed_out || !active) continue;
+    st_pkt(a.out + k, make_pkt(reduce_word<N, T, Acc>(w, (uint32_t)N, 0u), a.flag_out));
+  }
+}
+
+__global__ void __launch_bounds__(256) pack_k(const void* src, uint64_t* pkts, uint64_t nbytes,
+                                              uint32_t flag) {
+  const uint64_t npkt = (nbytes + 3) / 4;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < npkt; k += stride)
+    st_pkt(pkts + k, make_pkt(load_word(src, nbytes, k), flag));
+}
+
+__global__ void __launch_bounds__(256) unpack_k(const uint64_t* pkts, void* dst, uint64_t nbytes) {
+  const uint64_t npkt = (nbytes + 3) / 4;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < npkt; k += stride)
+    store_word(dst, nbytes, k, (uint32_t)pkts[k]);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+// (type, accumulator) pairs; the output type is the input type.
+#define MRR_PKT_PAIRS(X)                                                                  \
+  X(kF32, kF32) X(kF16, kF32) X(kF16, kF16) X(kBF16, kF32) X(kBF16, kBF16) X(kFP8, kF32) \
+  X(kFP8, kF16) X(kFP8, kFP8)
+
+#define MRR_PKT_RANKS(X, T, A) X(2, T, A) X(4, T, A) X(8, T, A) X(16, T, A) X(32, T, A)
+
+bool packet_supported(int nranks, int t, int tacc) {
+  if (!(nranks == 2 || nranks == 4 || nranks == 8 || nranks == 16 || nranks == 32)) return false;
+#define MRR_MATCH(T, A) if (t == T && tacc == A) return true;
+  MRR_PKT_PAIRS(MRR_MATCH)
+#undef MRR_MATCH
+  return false;
+}
+
+const void* packet_allpair_kernel(int nranks, int t, int tacc) {
+#define MRR_K(N, T, A) \
+  if (nranks == N && t == T && tacc == A) return (const void*)&packet_allpair_k<N, T, A>;
+#define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
+  MRR_PKT_PAIRS(MRR_ALLN)
+#undef MRR_ALLN
+#undef MRR_K
+  return nullptr;
+}
+
+hipError_t launch_packet_allpair(const PacketArgs& a, int nranks, int t, int tacc, int threads,
+                                 hipStream_t stream) {
+  const dim3 grid((uint32_t)nranks * a.nblocks), block((uint32_t)threads);
+#define MRR_K(N, T, A)                                                               \
+  if (nranks == N && t == T && tacc == A) {                                          \
+    hipLaunchKernelGGL((packet_allpair_k<N, T, A>), grid, block, 0, stream, a);      \
+    return hipGetLastError();                                                        \
+  }
+#define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
+  MRR_PKT_PAIRS(MRR_ALLN)
+#undef MRR_ALLN
+#undef MRR_K
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_packet_reduce(const PacketReduceArgs& a, int nranks, int t, int tacc,
+                                hipStream_t stream) {
+  uint64_t blocks = (a.npkts + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  const dim3 grid((uint32_t)blocks), block(256);
+#define MRR_K(N, T, A)                                                               \
+  if (nranks == N && t == T && tacc == A) {                                          \
+    hipLaunchKernelGGL((packet_reduce_k<N, T, A>), grid, block, 0, stream, a);       \
+    return hipGetLastError();                                                        \
+  }
+#define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
+  MRR_PKT_PAIRS(MRR_ALLN)
+#undef MRR_ALLN
+#undef MRR_K
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack(const void* src, uint64_t* pkts, size_t nbytes, uint32_t flag,
+                       hipStream_t stream) {
+  uint64_t blocks = ((nbytes + 3) / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(pack_k, dim3((uint32_t)blocks), dim3(256), 0, stream, src, pkts,
+                     (uint64_t)nbytes, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint64_t* pkts, void* dst, size_t nbytes, hipStream_t stream) {
+  uint64_t blocks = ((nbytes + 3) / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(unpack_k, dim3((uint32_t)blocks), dim3(256), 0, stream, pkts, dst,
+                     (uint64_t)nbytes);
+  return hipGetLastError();
+}
+
+}  // namespace mrr

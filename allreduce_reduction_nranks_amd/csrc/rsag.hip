@@ -1,0 +1,240 @@
+// rsag.hip -- RS/AG zero-copy N-rank reduction kernels for gfx950.
+//
+// Operation ("Support 2 ranks in AllreduceRsAgZeroCopy", MSCCL++ PR #948,
+// sections "why" and "what changed"): rank r reads chunk r of every rank's
+// input, reduces it, and writes the reduced chunk into every rank's output.
+// The kernel is generic in NRanks (NPeers = NRanks - 1) with the rank loops
+// unrolled at compile time, and exists for 2, 4, 8, 16 and 32 ranks.
+//
+// MI355X mapping.  All N rank buffers live in this GPU's HBM, so one launch
+// performs every rank's share (or one chosen rank's share).  The work is
+// HBM-bound (N*S bytes read, N*S written, ~N VALU adds per element), so the
+// design is about keeping enough 16-byte loads in flight:
+//   - workgroup g handles tile (g % tiles_per_chunk) of chunk
+//     first_chunk + g / tiles_per_chunk: the reduce-scatter partition, chunk
+//     by chunk;
+//   - each lane owns U 16-byte vectors of the tile (lane-contiguous, so every
+//     wave-level load and store instruction covers 1 KiB of one buffer);
+//   - all U*N loads are issued before any add (non-temporal: the data is
+//     touched once), then each vector is accumulated in rank order 0..N-1,
+//     narrowed once, and stored to all N outputs (the all-gather) with
+//     non-temporal 16-byte stores.
+// No __restrict__: an output may be its own rank's input (in place); a lane
+// reads every element it writes before writing it.
+#include "mrr_device.hpp"
+#include "mrr_internal.hpp"
+
+namespace mrr {
+
+constexpr int kRsagThreads = 256;
+
+// 16-byte vectors per lane per tile: enough independent loads in flight at
+// small N, bounded register use at large N.
+constexpr int rsag_unroll(int n, int tin) {
+  return tin == kFP8 ? (n <= 4 ? 2 : 1) : (n <= 2 ? 4 : (n <= 8 ? 2 : 1));
+}
+// Ranks whose vectors are loaded together before they are added: all of them
+// up to 16 ranks; groups of 16 (8 with an FP8 accumulator, whose per-element
+// rounding makes the unrolled body large) above that.
+constexpr int rsag_group(int n, int tacc) {
+  return tacc == kFP8 ? (n < 8 ? n : 8) : (n < 16 ? n : 16);
+}
+
+template <int In, int Acc, int Out>
+__device__ __forceinline__ void reduce_elem(const void* const* in, void* const* out, int n,
+                                            uint64_t i) {
+  float acc = round_acc<Acc>(load_elem<In>(in[0], i));
+  for (int r = 1; r < n; ++r) acc = round_acc<Acc>(acc + load_elem<In>(in[r], i));
+  for (int k = 0; k < n; ++k) store_elem<Out>(out[k], i, acc);
+}
+
+// Reduces UU vector positions v0 + u * kRsagThreads (u < UU) over the N ranks
+// and stores each result to all N outputs.  The first partial sum is x_0
+// rounded to the accumulator type (the identity except for an FP8
+// accumulator, which saturates an infinite x_0 like any later sum).  Ranks are taken in groups of G:
+// the group's UU * G loads are all issued before the first add of the group,
+// then the adds run in rank order.
+template <int N, int In, int Acc, int Out, int UU, int G>
+__device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
+  constexpr int VW = Vec<In>::VW;
+  constexpr int OV = Ty<Out>::size / Ty<In>::size;  // output vectors per input vector
+  constexpr int OW = Vec<Out>::VW;                  // elements per output vector
+  static_assert(N % G == 0, "rank group must divide N");
+  float acc[UU][VW];
+#pragma unroll(N / G <= 2 ? N / G : 1)
+  for (int g = 0; g < N; g += G) {
+    u32x4 raw[UU][G];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+#pragma unroll
+      for (int r = 0; r < G; ++r) raw[u][r] = ld_stream(a.in[g + r], v0 + (uint64_t)u * kRsagThreads);
+    }
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        float x[VW];
+        decode16<In>(raw[u][r], x);
+        if (g + r == 0) {
+#pragma unroll
+          for (int j = 0; j < VW; ++j) acc[u][j] = round_acc<Acc>(x[j]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < VW; ++j) acc[u][j] = round_acc<Acc>(acc[u][j] + x[j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UU; ++u) {
+    const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
+    u32x4 o[OV];
+#pragma unroll
+    for (int q = 0; q < OV; ++q) o[q] = encode16<Out>(acc[u] + q * OW);
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+#pragma unroll
+      for (int q = 0; q < OV; ++q) st_stream(a.out[k], v * OV + q, o[q]);
+    }
+  }
+}
+
+template <int N, int In, int Acc, int Out, int U>
+__global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a) {
+  constexpr int G = rsag_group(N, Acc);
+  const uint32_t chunk_rel = blockIdx.x / a.tiles_per_chunk;
+  const uint32_t tile = blockIdx.x - chunk_rel * a.tiles_per_chunk;
+  const uint64_t v_lo = (uint64_t)(a.first_chunk + chunk_rel) * a.chunk_vecs;
+  const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
+  const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
+
+  if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
+    reduce_store<N, In, Acc, Out, U, G>(a, v0);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
+      if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G>(a, v);
+    }
+  }
+  // Elements past the last whole vector (count % VW of them) go to the last
+  // workgroup, one per lane.
+  if (a.tail_count != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < a.tail_count)
+    reduce_elem<In, Acc, Out>(a.in, a.out, N, a.tail_begin + threadIdx.x);
+}
+
+// Element-wise variant for buffers that are not 16-byte aligned.
+template <int In, int Acc, int Out>
+__global__ void __launch_bounds__(256) rsag_scalar_kernel(const RsagScalarArgs a) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = a.begin + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.end; i += stride)
+    reduce_elem<In, Acc, Out>(a.in, a.out, a.nranks, i);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+#define MRR_RSAG_TRIPLES(X)                                                              \
+  X(kF32, kF32, kF32) X(kF16, kF32, kF16) X(kF16, kF16, kF16) X(kBF16, kF32, kBF16)      \
+  X(kBF16, kBF16, kBF16) X(kFP8, kF32, kFP8) X(kFP8, kF32, kF16) X(kFP8, kF32, kF32)     \
+  X(kFP8, kF16, kFP8) X(kFP8, kF16, kF16) X(kFP8, kF16, kF32) X(kFP8, kFP8, kFP8)        \
+  X(kFP8, kFP8, kF16) X(kFP8, kFP8, kF32)
+
+static bool valid_nranks(int n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32; }
+
+bool rsag_supported(int nranks, int tin, int tacc, int tout) {
+  if (!valid_nranks(nranks)) return false;
+#define MRR_MATCH(I, A, O) if (tin == I && tacc == A && tout == O) return true;
+  MRR_RSAG_TRIPLES(MRR_MATCH)
+#undef MRR_MATCH
+  return false;
+}
+
+static int type_size(int t) { return t == kF32 ? 4 : (t == kFP8 ? 1 : 2); }
+
+template <int In, int Acc, int Out>
+static void launch_vec_typed(int nranks, dim3 grid, const RsagArgs& a, hipStream_t s) {
+  const dim3 block(kRsagThreads);
+  switch (nranks) {
+#define MRR_CASE(N)                                                                        \
+  case N:                                                                                  \
+    hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In)>), grid, block, \
+                       0, s, a);                                                           \
+    break;
+    MRR_CASE(2) MRR_CASE(4) MRR_CASE(8) MRR_CASE(16) MRR_CASE(32)
+#undef MRR_CASE
+    default: break;
+  }
+}
+
+template <int In, int Acc, int Out>
+static void launch_scalar_typed(dim3 grid, const RsagScalarArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((rsag_scalar_kernel<In, Acc, Out>), grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const* outputs,
+                       hipStream_t stream) {
+  const int n = p.nranks;
+  const uint64_t vw = 16 / type_size(p.tin);
+  const uint64_t count = p.count;
+  // Chunk width: ceil(count / N) rounded up to whole 16-byte input vectors.
+  const uint64_t per = (count + n - 1) / n;
+  const uint64_t chunk_elems = (per + vw - 1) / vw * vw;
+
+  if (p.vector) {
+    RsagArgs a = {};
+    for (int r = 0; r < n; ++r) {
+      a.in[r] = inputs[r];
+      a.out[r] = outputs[r];
+    }
+    a.chunk_vecs = chunk_elems / vw;
+    a.total_vecs = count / vw;
+    a.tail_begin = a.total_vecs * vw;
+    const uint32_t tail = (uint32_t)(count - a.tail_begin);
+    const uint64_t tail_chunk = a.total_vecs / a.chunk_vecs;
+    const uint64_t tile_vecs = (uint64_t)kRsagThreads * rsag_unroll(n, p.tin);
+    a.tiles_per_chunk = (uint32_t)((a.chunk_vecs + tile_vecs - 1) / tile_vecs);
+    uint32_t nchunks;
+    if (p.rank < 0) {
+      a.first_chunk = 0;
+      nchunks = (uint32_t)n;
+      a.tail_count = tail;
+    } else {
+      a.first_chunk = (uint32_t)p.rank;
+      nchunks = 1;
+      a.tail_count = tail_chunk == (uint64_t)p.rank ? tail : 0;
+    }
+    const dim3 grid(nchunks * a.tiles_per_chunk);
+#define MRR_DISPATCH(I, A, O) \
+  if (p.tin == I && p.tacc == A && p.tout == O) launch_vec_typed<I, A, O>(n, grid, a, stream);
+    MRR_RSAG_TRIPLES(MRR_DISPATCH)
+#undef MRR_DISPATCH
+  } else {
+    RsagScalarArgs a = {};
+    for (int r = 0; r < n; ++r) {
+      a.in[r] = inputs[r];
+      a.out[r] = outputs[r];
+    }
+    a.nranks = n;
+    if (p.rank < 0) {
+      a.begin = 0;
+      a.end = count;
+    } else {
+      a.begin = chunk_elems * (uint64_t)p.rank;
+      a.end = a.begin + chunk_elems < count ? a.begin + chunk_elems : count;
+      if (a.begin > count) a.begin = count;
+    }
+    const uint64_t work = a.end - a.begin;
+    uint64_t blocks = (work + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks == 0) return hipSuccess;
+    const dim3 grid((uint32_t)blocks);
+#define MRR_DISPATCH(I, A, O) \
+  if (p.tin == I && p.tacc == A && p.tout == O) launch_scalar_typed<I, A, O>(grid, a, stream);
+    MRR_RSAG_TRIPLES(MRR_DISPATCH)
+#undef MRR_DISPATCH
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mrr

@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the N-rank reduction on one MI355X.
+
+Default workload (one "step" = one RS/AG zero-copy allreduce call over all
+ranks' chunks): 8 ranks x 64 MiB of f16 ~N(0,1) each, FP32 accumulation,
+every output written.  Inputs are resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c2]
+
+Prints ONE JSON line.  ``value`` is algorithmic HBM bytes per call
+(N * count * (e_in + e_out)) divided by the mean wall time per step; the
+``roofline`` object divides the same bytes by the kernel's mean duration
+measured with HIP events on the launch stream.  ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload.
+
+Other configurations (--config): c1 (2 x 1 MiB bf16), c3 (LL-packet allpair,
+8 ranks, --size KiB), c4 (8 x 32 MiB FP8 E4M3B15 -> f16 or fp8 via --out),
+c5 (N x 256 MiB bf16 via --nranks).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (and % of peak) for N-rank reduce at 64–256 MiB/rank"
+PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MiB = 1 << 20
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["allreduce_reduction_nranks_amd/csrc/rsag.hip",
+                  "allreduce_reduction_nranks_amd/csrc/mrr_device.hpp",
+                  "allreduce_reduction_nranks_amd/csrc/mrr_internal.hpp"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
+    None when it is missing or was taken on different kernel sources."""
+    path = os.path.join(PROFILE_DIR, "%s_pmc.txt" % workload_key)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 2 and not line.startswith("#"):
+            vals[parts[0]] = parts[1]
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """Times K back-to-back calls: host wall clock between synchronizations
+    (ms_per_step) and HIP events on the launch stream (kernel mean)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        wall_ms = (t1 - t0) * 1e3 / steps
+        kern_ms = e0.elapsed_time(e1) / steps
+        return wall_ms, kern_ms
+
+
+def copy_ceiling(torch, nbytes, steps=10):
+    """A plain device copy of nbytes (read nbytes + write nbytes) for context."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    wall, kern = Timer(torch).run(lambda: b.copy_(a), steps, 3)
+    del a, b
+    return 2 * nbytes / (kern * 1e-3) / 1e9
+
+
+def cpu_baseline_rsag(ins_dev, t, acc, tout, sample_elems):
+    """The oracle, as it stands, on the first sample_elems elements of every
+    rank (single thread)."""
+    import oracle
+    import synth
+    n = len(ins_dev)
+    sub = [synth.to_bits_numpy(x[:sample_elems]) for x in ins_dev]
+    oracle.default()  # build/load outside the timed region
+    t0 = time.perf_counter()
+    oracle.allreduce_all(sub, t, acc, tout)
+    dt = time.perf_counter() - t0
+    nbytes = n * sample_elems * (ESIZE[t] + ESIZE[tout])
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d elements of each of the %d ranks (%.1f%% of the workload), "
+                      "all %d outputs written, one thread, %.1f s"
+                      % (sample_elems, n, 100.0 * sample_elems / ins_dev[0].numel(), n, dt)}
+
+
+def bench_rsag(args, torch, mrr, synth):
+    if args.config == "c1":
+        n, t, per_rank = 2, "bf16", 1 * MiB
+        tout, acc = t, "f32"
+        kind = "normal"
+    elif args.config == "c4":
+        n, t, per_rank = 8, "fp8", 32 * MiB
+        tout, acc = args.out, "f32"
+        kind = "fp8codes"
+    elif args.config == "c5":
+        n, t, per_rank = args.nranks, "bf16", 256 * MiB
+        tout, acc = t, "f32"
+        kind = "normal"
+    else:
+        n, t, per_rank = 8, "f16", 64 * MiB
+        tout, acc = t, "f32"
+        kind = "normal"
+    count = per_rank // ESIZE[t]
+    gen_dev = "cuda" if n * count > (1 << 26) else "cpu"
+    log("config", args.config, "n", n, "type", t, "->", tout, "count", count, "inputs drawn on", gen_dev)
+    ins = [x.to("cuda") for x in synth.rank_inputs(kind, t, n, count, args.seed0, device=gen_dev)]
+    outs = [torch.empty(count * ESIZE[tout], dtype=torch.uint8, device="cuda") for _ in range(n)]
+    torch.cuda.synchronize()
+
+    def step():
+        st = mrr.mrr_allreduce_rsag_ex(ins, outs, count, t, acc, tout, n, -1)
+        if st != mrr.MRR_OK:
+            raise mrr.MrrError(st)
+
+    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    alg_bytes = n * count * (ESIZE[t] + ESIZE[tout])
+    value = alg_bytes / (wall_ms * 1e-3) / 1e9
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    key = {"c1": "rsag_2x1MiB_bf16", "c2": "rsag_8x64MiB_f16",
+           "c4": "rsag_8x32MiB_fp8_to_%s" % tout, "c5": "rsag_%dx256MiB_bf16" % n}[args.config]
+    traffic = measured_traffic(key)
+    ceiling = copy_ceiling(torch, n * count * ESIZE[t]) if args.copy_ceiling else None
+    workload = {"c1": "RS/AG allreduce, 2 ranks x 1 MiB bf16 ~N(0,1), fp32 accumulation",
+                "c2": "RS/AG zero-copy allreduce, 8 ranks x 64 MiB f16 ~N(0,1), fp32 accumulation, "
+                      "reduced chunks written to all 8 outputs",
+                "c4": "RS/AG allreduce, 8 ranks x 32 MiB FP8 E4M3B15 finite codes, fp32 "
+                      "accumulation, %s outputs" % tout,
+                "c5": "RS/AG allreduce, %d ranks x 256 MiB bf16 ~N(0,1), fp32 accumulation" % n}[
+        args.config]
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if acc == "f32" else acc,
+        "data": "synthetic (seeded, rank r drawn with seed %d + r)" % args.seed0,
+        "config": {"workload": workload, "nranks": n, "bytes_per_rank": count * ESIZE[t],
+                   "count": count, "in": t, "accum": acc, "out": tout,
+                   "algorithmic_bytes_per_call": alg_bytes, "kernel_us": round(kern_ms * 1e3, 2),
+                   "pct_of_hbm_peak": round(100 * value / PEAK_GBPS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": traffic},
+    }
+    if ceiling is not None:
+        result["config"]["copy_ceiling_gbps"] = round(ceiling, 2)
+    if args.cpu_baseline:
+        sample = min(count, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline_rsag(ins, t, acc, tout, sample)
+    return result
+
+
+def bench_packet(args, torch, mrr, synth):
+    n, t = 8, "f16"
+    count = args.size * 1024 // 2
+    ins = [x.to("cuda") for x in synth.rank_inputs("uniform", t, n, count, args.seed0)]
+    outs = [torch.empty(count, dtype=torch.float16, device="cuda") for _ in range(n)]
+    sbytes = mrr.mrr_packet_scratch_bytes(count, t, n)
+    scratch = torch.zeros(sbytes // 8, dtype=torch.int64, device="cuda")
+    flags = torch.zeros(n * mrr.PKT_FLAG_SLOTS, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step():
+        st = mrr.mrr_allreduce_packet_ex(ins, outs, scratch, sbytes, flags, count, t, "f32", n,
+                                         4_000_000, err, args.blocks, args.threads)
+        if st != mrr.MRR_OK:
+            raise mrr.MrrError(st)
+
+    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    if int(err.item()) != 0:
+        raise RuntimeError("packet poll timed out")
+    S = count * 2
+    alg_bytes = 3 * n * S + 4 * n * (n - 1) * S
+    return {
+        "metric": "LL-packet allpair allreduce latency", "value": round(kern_ms * 1e3, 3),
+        "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic ~U(-1,1)",
+        "config": {"workload": "LL-packet allpair allreduce, 8 ranks x %d KiB f16" % args.size,
+                   "nranks": n, "bytes_per_rank": S, "blocks_per_rank": args.blocks,
+                   "threads": args.threads, "algorithmic_bytes_per_call": alg_bytes,
+                   "algorithmic_gbps": round(alg_bytes / (kern_ms * 1e-3) / 1e9, 2)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--nranks", type=int, default=8, help="c5: rank count")
+    ap.add_argument("--out", default="f16", choices=["f16", "fp8", "f32"], help="c4: output type")
+    ap.add_argument("--size", type=int, default=1024, help="c3: KiB per rank")
+    ap.add_argument("--blocks", type=int, default=0, help="c3: blocks per rank (0 = auto)")
+    ap.add_argument("--threads", type=int, default=0, help="c3: threads (0 = auto)")
+    ap.add_argument("--seed0", type=int, default=0)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 30,
+                    help="elements per rank the CPU oracle baseline reduces")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--no-copy-ceiling", dest="copy_ceiling", action="store_false")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the N rank buffers live in one MI355X's HBM, "
+              "so --gpus %d is not a configuration this build runs" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import allreduce_reduction_nranks_amd as mrr
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mrr.load_library()
+    if args.config == "c3":
+        result = bench_packet(args, torch, mrr, synth)
+    else:
+        result = bench_rsag(args, torch, mrr, synth)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * mrr.h -- libmrr: N-rank allreduce reduction for AMD MI355X (gfx950).
+ *
+ * One GPU holds the N "rank" buffers in its own HBM; each call performs every
+ * rank's share of the reduction (or one chosen rank's share) in HIP kernels.
+ *
+ * Operations, and the passages that define them:
+ *   - RS/AG zero-copy allreduce: "Support 2 ranks in AllreduceRsAgZeroCopy"
+ *     (MSCCL++ PR #948), sections "why" and "what changed": rank r reduces
+ *     chunk r of every rank's input and writes the result straight into every
+ *     rank's output, with no scratch; the kernel is generic in NRanks
+ *     (NPeers = NRanks - 1, peer loops unrolled at compile time) and exists
+ *     for 2, 4, 8, 16 and 32 ranks; any other rank count is refused.
+ *   - LL-packet allpair allreduce: MSCCL++ commit history (/src), entry fixing
+ *     the allreduce_allpair_packet algorithm: packets go to a scratch area so
+ *     the input is never overwritten, one workgroup sends, reduces and writes
+ *     back, block/thread counts are validated, and the flag update works when
+ *     a workgroup has fewer threads than flags.  Entry on the default flag
+ *     buffer: one flag buffer shared by all algorithms so that switching
+ *     between them by message size cannot hang.
+ *   - FP8 E4M3B15 and accumulation precision: MSCCL++ commit history, entries
+ *     adding the fp8_e4m3b15 datatype (4 exponent bits, 3 mantissa bits,
+ *     bias 15, largest finite value 0.9375, converted through fp16) and the
+ *     accumDtype parameter (AUTO resolves to the input type), and the entry
+ *     adding ROCm support for the type with FP16/FP32 accumulation.
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers on the calling thread's current
+ *     HIP device.  Pointer arrays (inputs[], outputs[], in_pkts[]) are HOST
+ *     arrays of nranks device pointers; they are copied into the kernel
+ *     arguments, so the host arrays may be reused as soon as the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call is stream-ordered and asynchronous: it validates its
+ *     arguments on the host, launches, and returns without synchronising.
+ *     No call allocates or frees memory, so calls may be captured in a HIP
+ *     graph.
+ *   - The caller owns every buffer.  The library keeps no device state; it
+ *     caches only per-device properties (CU count, occupancy).
+ *   - Validation happens before any launch: on an error nothing is launched
+ *     and the specific status is returned.  MRR_LOG=1 in the environment
+ *     prints one stderr line per refused call.
+ *   - count == 0 (or n == 0) returns MRR_OK without launching.
+ *   - Element types travel as raw bits: f16 / bf16 as 16-bit IEEE binary16 /
+ *     bfloat16, FP8 E4M3B15 as one byte (sign, 4-bit exponent with bias 15,
+ *     3-bit mantissa; exponent 15 encodes inf (mantissa 0) and NaN).
+ *   - Rounding is IEEE round-to-nearest-even everywhere.  f16 / bf16 overflow
+ *     gives +-inf; FP8 E4M3B15 saturates to +-0.9375 (also from +-inf); NaN
+ *     gives NaN (FP8: 0x7F with the input's sign).  Denormals are kept.
+ */
+#ifndef MRR_H
+#define MRR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mrr_status {
+  MRR_OK = 0,
+  MRR_EINVAL = 1,       /* bad argument: null pointer, rank or geometry out of range */
+  MRR_EUNSUPPORTED = 2, /* rank count or type combination not provided */
+  MRR_EALIGN = 3,       /* a pointer not aligned as the entry point requires */
+  MRR_EOVERLAP = 4,     /* an output overlaps another buffer other than its own input */
+  MRR_ESCRATCH = 5,     /* packet scratch smaller than mrr_packet_scratch_bytes() */
+  MRR_ETIMEDOUT = 6,    /* (device error word only) a packet poll exceeded max_spins */
+  MRR_EHIP = 7          /* the HIP runtime refused the launch */
+} mrr_status;
+
+typedef enum mrr_dtype {
+  MRR_AUTO = 0, /* accumulation: the input type; output: the input type */
+  MRR_F32 = 1,
+  MRR_F16 = 2,
+  MRR_BF16 = 3,
+  MRR_FP8_E4M3B15 = 4
+} mrr_dtype;
+
+/* Largest rank count any entry point accepts. */
+#define MRR_MAX_RANKS 32
+/* Flag slots per rank in a packet flag buffer. */
+#define MRR_PKT_FLAG_SLOTS 1024
+
+/* --------------------------------------------------------------------------
+ * RS/AG zero-copy allreduce ("Support 2 ranks in AllreduceRsAgZeroCopy",
+ * sections "why" and "what changed").
+ *
+ * For every k < nranks and i < count:
+ *   outputs[k][i] = round_out( x_0[i] + x_1[i] + ... + x_{nranks-1}[i] )
+ * summed in rank order 0..nranks-1 starting from x_0 (so -0 sums stay -0).
+ * The index space is split into nranks chunks of
+ *   C = roundup(ceil(count / nranks), 16 / sizeof(input element))
+ * elements (the last chunk may be short or empty); chunk r is rank r's
+ * reduce-scatter share, and its reduced values are written to all nranks
+ * outputs (the all-gather).  The result does not depend on the partition.
+ *
+ * mrr_allreduce_rsag: input type == output type == dtype (F32, F16, BF16 or
+ *   FP8_E4M3B15), FP32 accumulation, every chunk.
+ * mrr_allreduce_rsag_ex:
+ *   in     F32 | F16 | BF16 | FP8_E4M3B15
+ *   accum  AUTO (= in) | F32 | F16 (F16 and FP8 inputs) | BF16 (BF16 inputs) |
+ *          FP8_E4M3B15 (FP8 inputs).  With a non-F32 accumulator every
+ *          partial sum is rounded to that type.
+ *   out    AUTO (= in); FP8 inputs may also produce F16 or F32.
+ *   rank   -1: all chunks (every rank's share); 0..nranks-1: chunk `rank`
+ *          only, i.e. one GPU's share at its real shape (reads count/nranks
+ *          elements of every input, writes them to every output).
+ *
+ * Buffers: inputs[r] holds count input elements, outputs[k] room for count
+ * output elements.  outputs[k] may be exactly inputs[k] (in place; only when
+ * the input and output types have the same size); any other overlap between
+ * an output and any buffer gives MRR_EOVERLAP.  Inputs may overlap each
+ * other.  Pointers must be aligned to their element size (MRR_EALIGN);
+ * 16-byte alignment of every pointer selects the vector kernels, otherwise a
+ * slower element-wise kernel runs.
+ * Errors: MRR_EUNSUPPORTED for nranks not in {2,4,8,16,32} or a type
+ * combination not listed; MRR_EINVAL for null arrays/pointers or a rank
+ * outside [-1, nranks); MRR_EHIP when the launch fails.
+ * ------------------------------------------------------------------------ */
+mrr_status mrr_allreduce_rsag(const void* const* inputs, void* const* outputs, size_t count,
+                              mrr_dtype dtype, int nranks, void* stream);
+
+mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs, size_t count,
+                                 mrr_dtype in, mrr_dtype accum, mrr_dtype out, int nranks,
+                                 int rank, void* stream);
+
+/* --------------------------------------------------------------------------
+ * LL-packet allpair allreduce (commit history: allreduce_allpair_packet fix;
+ * default flag buffer entry).
+ *
+ * A packet is 8 bytes: payload word k of a rank's buffer (bytes [4k, 4k+4),
+ * little-endian, bytes past the end read as zero) in the low 32 bits and a
+ * 32-bit flag in the high 32 bits.  npkt = ceil(count * elem_size / 4).
+ *
+ * Each call takes F = (flag slot value) + 1, skipping 0 on 32-bit wrap.
+ * Workgroup (rank d, block b) packs slice b of inputs[d] and stores the
+ * packets into scratch[p][d][*] for every peer p != d (64-bit agent-scope
+ * stores); it then polls scratch[d][s][*] of slice b for every s != d until
+ * every packet carries F (wavefront-level vote, 64-bit agent-scope loads),
+ * sums in rank order 0..nranks-1 -- taking its own contribution straight
+ * from inputs[d] -- and writes slice b of outputs[d]; finally it sets every
+ * flag slot j of rank d with j % B == b to F.  The inputs are never written.
+ *
+ * scratch:  device, 8-byte aligned, layout [dst][src][npkt] of uint64 packets,
+ *           at least mrr_packet_scratch_bytes() bytes (else MRR_ESCRATCH);
+ *           the self slots [d][d] are unused.  Zero it once before first use.
+ * flags:    device, nranks * MRR_PKT_FLAG_SLOTS uint32, zero-filled once
+ *           before first use (and whenever it is recycled).  Every call leaves
+ *           every slot equal to the F it used, so count, geometry and the
+ *           algorithm may change between calls without a hang, and graph
+ *           replays advance F on the device.  All ranks' slots must hold the
+ *           same value.  May be shared with later calls of any packet entry.
+ * inputs / outputs: device, 4-byte aligned (MRR_EALIGN), outputs[k] may be
+ *           inputs[k] exactly; other overlaps give MRR_EOVERLAP.
+ * dtype:    F32 | F16 | BF16 | FP8_E4M3B15 (output type == input type).
+ * accum:    AUTO (= dtype) | F32 | F16 (F16 and FP8 data).
+ * max_spins: bound on poll iterations per wavefront; on expiry the kernel
+ *           writes MRR_ETIMEDOUT into *dev_err (if dev_err is not NULL; first
+ *           error wins) and finishes; outputs are then undefined.  0 = no
+ *           bound.  Read *dev_err after synchronising the stream.
+ * blocks_per_rank / threads (_ex only): B and the workgroup size; 0 = auto.
+ *           B must be in [1, MRR_PKT_FLAG_SLOTS]; threads a multiple of 64 in
+ *           [64, 1024]; nranks * B workgroups must fit on the GPU at once
+ *           (every workgroup waits for its peers), else MRR_EINVAL.
+ * Calls that overlap in time on the same scratch or flags race; calls on one
+ * stream never overlap.
+ * ------------------------------------------------------------------------ */
+size_t mrr_packet_scratch_bytes(size_t count, mrr_dtype dtype, int nranks);
+size_t mrr_packet_flag_bytes(int nranks);
+
+mrr_status mrr_allreduce_packet(const void* const* inputs, void* const* outputs, void* scratch,
+                                size_t scratch_bytes, uint32_t* flags, size_t count,
+                                mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                uint32_t max_spins, uint32_t* dev_err, void* stream);
+
+mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outputs, void* scratch,
+                                   size_t scratch_bytes, uint32_t* flags, size_t count,
+                                   mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                   uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
+                                   int threads, void* stream);
+
+/* Receive step alone: for every k < npkts, wait until in_pkts[s][k] carries
+ * flag_in for every s, sum the payload elements (4 / elem_size per word) in
+ * rank order with accumulator accum, round to dtype and store
+ * out_pkts[k] = (flag_out << 32) | word with a 64-bit agent-scope store.
+ * in_pkts: host array of nranks device pointers (8-byte aligned); out_pkts
+ * must not overlap them.  max_spins / dev_err as above.  No co-residency is
+ * needed (the producers are outside the call), so any npkts works. */
+mrr_status mrr_packet_reduce(const uint64_t* const* in_pkts, uint64_t* out_pkts, size_t npkts,
+                             mrr_dtype dtype, mrr_dtype accum, int nranks, uint32_t flag_in,
+                             uint32_t flag_out, uint32_t max_spins, uint32_t* dev_err,
+                             void* stream);
+
+/* pkts[k] = (flag << 32) | word_k(src) for k < ceil(nbytes / 4) (64-bit
+ * agent-scope stores).  src: 4-byte aligned device buffer of nbytes bytes;
+ * pkts: 8-byte aligned. */
+mrr_status mrr_pack(const void* src, uint64_t* pkts, size_t nbytes, uint32_t flag, void* stream);
+/* Writes the nbytes payload bytes of pkts into dst (4-byte aligned). */
+mrr_status mrr_unpack(const uint64_t* pkts, void* dst, size_t nbytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * FP8 E4M3B15 codec (commit history: fp8_e4m3b15 datatype entry).
+ * Decode is exact; encode rounds once, to nearest-even, saturating at
+ * +-0.9375.  n elements; pointers aligned to their element size (MRR_EALIGN),
+ * 16-byte alignment selects the vector kernels.  In and out must not overlap
+ * (MRR_EOVERLAP).
+ * ------------------------------------------------------------------------ */
+mrr_status mrr_fp8b15_to_f16(const uint8_t* in, uint16_t* out, size_t n, void* stream);
+mrr_status mrr_fp8b15_to_f32(const uint8_t* in, float* out, size_t n, void* stream);
+mrr_status mrr_f16_to_fp8b15(const uint16_t* in, uint8_t* out, size_t n, void* stream);
+mrr_status mrr_f32_to_fp8b15(const float* in, uint8_t* out, size_t n, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mrr_status_string(mrr_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int mrr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MRR_H */

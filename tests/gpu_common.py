@@ -1,0 +1,59 @@
+"""Helpers shared by the GPU parity tests: device buffers, bit-level
+comparison against the oracle, and progress prints that name each case
+before it touches the GPU."""
+import sys
+
+import numpy as np
+import torch
+
+import synth
+
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8}
+SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+
+
+def announce(*what):
+    print("[gpu case]", *what, file=sys.stderr, flush=True)
+
+
+def bits(x: torch.Tensor) -> np.ndarray:
+    return synth.to_bits_numpy(x)
+
+
+def is_nan_bits(a: np.ndarray, t: str) -> np.ndarray:
+    a = np.asarray(a)
+    if t == "f32":
+        u = a.view(np.uint32)
+        return (u & 0x7FFFFFFF) > 0x7F800000
+    if t == "f16":
+        return (a.view(np.uint16) & 0x7FFF) > 0x7C00
+    if t == "bf16":
+        return (a.view(np.uint16) & 0x7FFF) > 0x7F80
+    return (a.view(np.uint8) & 0x7F) > 0x78
+
+
+def assert_bits_equal(got: np.ndarray, want: np.ndarray, t: str, what: str = ""):
+    """Bit-exact equality; NaN positions only need to be NaN on both sides."""
+    g = np.ascontiguousarray(got)
+    w = np.ascontiguousarray(want)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    view = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}[t]
+    gn, wn = is_nan_bits(g, t), is_nan_bits(w, t)
+    assert np.array_equal(gn, wn), "%s: NaN positions differ" % what
+    bad = np.nonzero((g.view(view) != w.view(view)) & ~wn)[0]
+    assert bad.size == 0, "%s: %d mismatches, first at %s: got %s want %s" % (
+        what, bad.size, bad[:4], g.view(view)[bad[:4]], w.view(view)[bad[:4]])
+
+
+def empty(t: str, count: int, fill=None) -> torch.Tensor:
+    x = torch.empty(count, dtype=TORCH[t], device="cuda")
+    if fill is not None:
+        x.view(torch.uint8).fill_(fill)
+    return x
+
+
+def inputs_for(t: str, n: int, count: int, seed0: int, kind=None, device="cuda"):
+    kind = kind or ("fp8codes" if t == "fp8" else "normal")
+    return [x.to(device) for x in synth.rank_inputs(kind, t, n, count, seed0, device="cpu")] \
+        if device == "cuda" and count * n <= (1 << 24) else \
+        synth.rank_inputs(kind, t, n, count, seed0, device=device)

@@ -1,0 +1,189 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point that
+include/mrr.h declares, and refuses bad arguments with the documented status
+before touching the GPU.  Pointers here are fake device addresses that the
+library never dereferences on these paths."""
+import os
+import re
+
+import pytest
+
+import allreduce_reduction_nranks_amd as mrr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mrr.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+BASE = 0x7F0000000000  # fake, 4 KiB aligned device address space
+MiB = 1 << 20
+
+
+def fake(i, size=64 * MiB, off=0):
+    return BASE + i * size + off
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mrr_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mrr.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        txt = mrr.mrr_status_string(s)
+        assert txt.startswith(mrr.STATUS_NAMES[s])
+    assert "unknown" in mrr.mrr_status_string(99)
+    assert mrr.mrr_version() >= 10000
+
+
+def read_golden(name):
+    out = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            out[k] = [int(x) for x in v]
+    return out
+
+
+def rsag(n, count=1024, t="f16", acc="f32", out=None, rank=-1, ins=None, outs=None):
+    ins = ins if ins is not None else [fake(r) for r in range(n)]
+    outs = outs if outs is not None else [fake(64 + r) for r in range(n)]
+    return mrr.mrr_allreduce_rsag_ex(ins, outs, count, t, acc, out or t, n, rank, stream=0)
+
+
+def test_rank_counts_follow_the_pages(lib):
+    g = read_golden("rsag_verification_sizes.txt")
+    for n in g["rejected_nranks"] + [0, 1, 33, 64, -2]:
+        assert rsag(max(n, 0) if n > 0 else n, ins=[fake(r) for r in range(max(n, 1))],
+                    outs=[fake(64 + r) for r in range(max(n, 1))]) == mrr.MRR_EUNSUPPORTED
+    for n in g["supported_nranks"]:
+        assert rsag(n, count=0) == mrr.MRR_OK  # nothing to do: no launch
+
+
+def test_rsag_argument_checks(lib):
+    assert rsag(8, rank=-2) == mrr.MRR_EINVAL
+    assert rsag(8, rank=8) == mrr.MRR_EINVAL
+    assert mrr.load_library().mrr_allreduce_rsag_ex(None, None, 16, 2, 1, 2, 8, -1, None) \
+        == mrr.MRR_EINVAL
+    ins = [fake(r) for r in range(8)]
+    ins[3] = 0
+    assert rsag(8, ins=ins) == mrr.MRR_EINVAL
+
+
+@pytest.mark.parametrize("t,acc,out", [("bf16", "f16", "bf16"), ("f16", "bf16", "f16"),
+                                       ("f32", "f16", "f32"), ("f16", "f32", "f32"),
+                                       ("bf16", "f32", "f16"), ("f32", "f32", "fp8")])
+def test_rsag_unsupported_types(lib, t, acc, out):
+    assert rsag(8, t=t, acc=acc, out=out) == mrr.MRR_EUNSUPPORTED
+
+
+def test_rsag_alignment(lib):
+    ins = [fake(r) for r in range(4)]
+    ins[2] += 1  # odd address for f16
+    assert rsag(4, ins=ins) == mrr.MRR_EALIGN
+    outs = [fake(64 + r) for r in range(4)]
+    outs[1] += 2  # f32 needs 4
+    assert rsag(4, t="f32", outs=outs) == mrr.MRR_EALIGN
+
+
+def test_rsag_overlap(lib):
+    ins = [fake(r) for r in range(4)]
+    # output 0 overlaps input 1 partially
+    assert rsag(4, count=1024, ins=ins, outs=[fake(1, off=512)] + [fake(64 + r) for r in range(1, 4)]) \
+        == mrr.MRR_EOVERLAP
+    # output 2 equals input 1 exactly: only an output's own input may alias it
+    outs = [fake(64 + r) for r in range(4)]
+    outs[2] = ins[1]
+    assert rsag(4, ins=ins, outs=outs) == mrr.MRR_EOVERLAP
+    # two outputs overlap
+    outs = [fake(64 + r) for r in range(4)]
+    outs[3] = outs[2] + 16
+    assert rsag(4, ins=ins, outs=outs) == mrr.MRR_EOVERLAP
+    # fp8 -> f16 in place is impossible (sizes differ)
+    assert rsag(4, t="fp8", acc="f32", out="f16", ins=ins, outs=list(ins)) == mrr.MRR_EOVERLAP
+
+
+def test_packet_sizes(lib):
+    assert mrr.mrr_packet_scratch_bytes(1000, "f16", 8) == 8 * 8 * 500 * 8
+    assert mrr.mrr_packet_scratch_bytes(1023, "fp8", 4) == 4 * 4 * 256 * 8
+    assert mrr.mrr_packet_scratch_bytes(7, "f32", 2) == 2 * 2 * 7 * 8
+    assert mrr.mrr_packet_flag_bytes(8) == 8 * 1024 * 4
+    assert mrr.mrr_packet_flag_bytes(0) == 0
+
+
+def packet(n=8, count=4096, t="f16", acc="f32", scratch=None, sbytes=None, flags=None,
+           blocks=0, threads=0, ins=None, outs=None):
+    ins = ins if ins is not None else [fake(r) for r in range(n)]
+    outs = outs if outs is not None else [fake(64 + r) for r in range(n)]
+    scratch = scratch if scratch is not None else fake(200)
+    sbytes = sbytes if sbytes is not None else mrr.mrr_packet_scratch_bytes(count, t, n)
+    flags = flags if flags is not None else fake(300)
+    return mrr.mrr_allreduce_packet_ex(ins, outs, scratch, sbytes, flags, count, t, acc, n,
+                                       1000, 0, blocks, threads, stream=0)
+
+
+def test_packet_argument_checks(lib):
+    assert packet(n=3) == mrr.MRR_EUNSUPPORTED
+    assert packet(t="bf16", acc="f16") == mrr.MRR_EUNSUPPORTED
+    assert packet(sbytes=mrr.mrr_packet_scratch_bytes(4096, "f16", 8) - 8) == mrr.MRR_ESCRATCH
+    assert packet(threads=100) == mrr.MRR_EINVAL
+    assert packet(threads=2048) == mrr.MRR_EINVAL
+    assert packet(blocks=1025) == mrr.MRR_EINVAL
+    assert packet(scratch=fake(200, off=4)) == mrr.MRR_EALIGN
+    ins = [fake(r) for r in range(8)]
+    ins[5] += 2
+    assert packet(ins=ins) == mrr.MRR_EALIGN
+    assert packet(flags=fake(200, off=64)) == mrr.MRR_EOVERLAP  # flags inside scratch
+    assert packet(scratch=fake(3)) == mrr.MRR_EOVERLAP  # scratch over an input
+    assert packet(count=0) == mrr.MRR_OK
+
+
+def test_packet_reduce_and_pack_checks(lib):
+    ins = [fake(r) for r in range(4)]
+    L = mrr
+    assert L.mrr_packet_reduce(ins, fake(100), 64, "f16", "f32", 5, 1, 2, 10, None, 0) \
+        == mrr.MRR_EUNSUPPORTED
+    assert L.mrr_packet_reduce(ins, fake(100, off=4), 64, "f16", "f32", 4, 1, 2, 10, None, 0) \
+        == mrr.MRR_EALIGN
+    assert L.mrr_packet_reduce(ins, fake(1, off=64), 64, "f16", "f32", 4, 1, 2, 10, None, 0) \
+        == mrr.MRR_EOVERLAP
+    assert L.mrr_packet_reduce(ins, fake(100), 0, "f16", "f32", 4, 1, 2, 10, None, 0) == mrr.MRR_OK
+    assert L.mrr_pack(fake(0, off=2), fake(1), 100, 1, 0) == mrr.MRR_EALIGN
+    assert L.mrr_pack(fake(0), fake(0, off=64), 100, 1, 0) == mrr.MRR_EOVERLAP
+    assert L.mrr_unpack(fake(0, off=4), fake(1), 100, 0) == mrr.MRR_EALIGN
+    assert L.mrr_pack(0, fake(1), 100, 1, 0) == mrr.MRR_EINVAL
+    assert L.mrr_pack(fake(0), fake(1), 0, 1, 0) == mrr.MRR_OK
+
+
+def test_codec_checks(lib):
+    assert mrr.mrr_fp8b15_to_f16(fake(0), fake(1, off=1), 16, 0) == mrr.MRR_EALIGN
+    assert mrr.mrr_f32_to_fp8b15(fake(0, off=2), fake(1), 16, 0) == mrr.MRR_EALIGN
+    assert mrr.mrr_fp8b15_to_f32(fake(0), fake(0, off=8), 16, 0) == mrr.MRR_EOVERLAP
+    assert mrr.mrr_f16_to_fp8b15(0, fake(1), 16, 0) == mrr.MRR_EINVAL
+    assert mrr.mrr_f16_to_fp8b15(fake(0), fake(1), 0, 0) == mrr.MRR_OK
+
+
+def test_binding_names_match_header():
+    names = declared_functions()
+    for n in names:
+        assert callable(getattr(mrr, n)), n
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "allreduce_reduction_nranks_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.lower(), f

@@ -1,0 +1,241 @@
+"""GPU parity of the RS/AG zero-copy reduction against the CPU oracle.
+
+Every comparison is bit-exact (0 mismatches); NaN positions only need to be
+NaN on both sides.  Small cases span several workgroup tiles per chunk and a
+ragged tail; the full-size cases run the exact launch bench.py times."""
+import numpy as np
+import pytest
+import torch
+
+import allreduce_reduction_nranks_amd as mrr
+import oracle
+from gpu_common import TORCH, announce, assert_bits_equal, bits, empty, inputs_for
+
+pytestmark = pytest.mark.gpu
+
+RANKS = [2, 4, 8, 16, 32]
+TRIPLES = [("f32", "f32", "f32"), ("f16", "f32", "f16"), ("f16", "f16", "f16"),
+           ("bf16", "f32", "bf16"), ("bf16", "bf16", "bf16"),
+           ("fp8", "f32", "fp8"), ("fp8", "f32", "f16"), ("fp8", "f32", "f32"),
+           ("fp8", "f16", "fp8"), ("fp8", "f16", "f16"), ("fp8", "f16", "f32"),
+           ("fp8", "fp8", "fp8"), ("fp8", "fp8", "f16"), ("fp8", "fp8", "f32")]
+VW = {"f32": 4, "f16": 8, "bf16": 8, "fp8": 16}
+
+
+def run(ins, t, acc, tout, rank=-1, outs=None, fill=0xA5):
+    n, count = len(ins), ins[0].numel()
+    outs = outs if outs is not None else [empty(tout, count, fill) for _ in range(n)]
+    st = mrr.mrr_allreduce_rsag_ex(ins, outs, count, t, acc, tout, n, rank)
+    assert st == mrr.MRR_OK, mrr.mrr_status_string(st)
+    torch.cuda.synchronize()
+    return outs
+
+
+def check_all(outs, want, tout, what):
+    for k, o in enumerate(outs):
+        assert_bits_equal(bits(o), want, tout, "%s out[%d]" % (what, k))
+
+
+@pytest.mark.parametrize("n", RANKS)
+@pytest.mark.parametrize("t,acc,tout", TRIPLES, ids=["-".join(x) for x in TRIPLES])
+def test_parity_small(n, t, acc, tout):
+    # several tiles of 256 lanes x up to 4 vectors per chunk, plus a ragged tail
+    count = n * 3 * 256 * 2 * VW[t] + 13
+    announce("rsag small", n, t, acc, tout, count)
+    ins = inputs_for(t, n, count, seed0=10 * n)
+    outs = run(ins, t, acc, tout)
+    want = oracle.allreduce([bits(x) for x in ins], t, acc, tout)
+    check_all(outs, want, tout, "n=%d %s/%s/%s" % (n, t, acc, tout))
+
+
+@pytest.mark.parametrize("t", ["f32", "f16", "bf16", "fp8"])
+@pytest.mark.parametrize("count", [1, 3, 7, 8, 9, 15, 16, 17, 31, 33, 127, 129, 4095, 4097])
+def test_edge_counts(t, count):
+    n = 8
+    announce("rsag edge", t, count)
+    ins = inputs_for(t, n, count, seed0=count)
+    outs = run(ins, t, "f32", t)
+    want = oracle.allreduce([bits(x) for x in ins], t, "f32", t)
+    check_all(outs, want, t, "count=%d" % count)
+
+
+def test_two_rank_bf16_one_mib():
+    """2 ranks, 1 MiB of bf16 each (524288 elements) ~N(0,1), seeds 0 and 1."""
+    announce("rsag 2x1MiB bf16")
+    ins = inputs_for("bf16", 2, 524288, seed0=0)
+    outs = [empty("bf16", 524288) for _ in range(2)]
+    assert mrr.mrr_allreduce_rsag(ins, outs, 524288, "bf16", 2) == mrr.MRR_OK
+    torch.cuda.synchronize()
+    check_all(outs, oracle.allreduce([bits(x) for x in ins], "bf16", "f32"), "bf16", "2x1MiB")
+
+
+@pytest.mark.parametrize("n", [2, 8, 32])
+def test_rank_share_writes_only_its_chunk(n):
+    t, count = "f16", n * 1000 + 5
+    announce("rsag rank share", n)
+    ins = inputs_for(t, n, count, seed0=77)
+    want = oracle.allreduce([bits(x) for x in ins], t, "f32", t)
+    per = -(-count // n)
+    chunk = -(-per // VW[t]) * VW[t]
+    for r in range(n):
+        outs = run(ins, t, "f32", t, rank=r, fill=0x5A)
+        lo, hi = min(r * chunk, count), min((r + 1) * chunk, count)
+        for k, o in enumerate(outs):
+            b = bits(o)
+            assert_bits_equal(b[lo:hi], want[lo:hi], t, "rank %d out %d" % (r, k))
+            untouched = np.concatenate([b[:lo], b[hi:]]).view(np.uint8)
+            assert np.all(untouched == 0x5A), "rank %d wrote outside its chunk" % r
+
+
+@pytest.mark.parametrize("t", ["f16", "bf16", "f32", "fp8"])
+def test_in_place(t):
+    n, count = 8, 50021
+    announce("rsag in place", t)
+    ins = inputs_for(t, n, count, seed0=5)
+    want = oracle.allreduce([bits(x) for x in ins], t, "f32", t)
+    run(ins, t, "f32", t, outs=ins)
+    check_all(ins, want, t, "in place")
+
+
+@pytest.mark.parametrize("t,off", [("f16", 1), ("bf16", 3), ("f32", 1), ("fp8", 5)])
+def test_unaligned_buffers_use_elementwise_path(t, off):
+    n, count = 4, 20000
+    announce("rsag unaligned", t, off)
+    base = inputs_for(t, n, count + off, seed0=9)
+    ins = [x[off:] for x in base]
+    outs = [empty(t, count + off)[off:] for _ in range(n)]
+    run(ins, t, "f32", t, outs=outs)
+    want = oracle.allreduce([bits(x) for x in ins], t, "f32", t)
+    check_all(outs, want, t, "unaligned")
+
+
+def test_special_values():
+    n = 4
+    # -0, +0, inf, -inf, NaN, subnormals, overflow, cancellation
+    f16 = np.array([0x8000, 0x0000, 0x7C00, 0xFC00, 0x7E00, 0x0001, 0x03FF, 0x7BFF, 0x3C00,
+                    0xBC00, 0x8001, 0x0200] * 37, np.uint16)
+    rng = np.random.default_rng(3)
+    cols = [np.roll(f16, s) if s else f16 for s in range(n)]
+    cols[3] = rng.permutation(cols[3])
+    for t in ("f16", "bf16"):
+        announce("rsag special", t)
+        ins = [torch.from_numpy(c.view(np.int16).copy()).view(TORCH[t]).cuda() for c in cols]
+        for acc in ("f32", t):
+            outs = run(ins, t, acc, t)
+            check_all(outs, oracle.allreduce(cols, t, acc, t), t, "special %s/%s" % (t, acc))
+    f32 = np.array([-0.0, 0.0, np.inf, -np.inf, np.nan, 1e-45, 3e38, 3e38, -1e-40, 1.0],
+                   np.float32)
+    cols = [np.roll(f32, s) for s in range(n)]
+    ins = [torch.from_numpy(c.copy()).cuda() for c in cols]
+    outs = run(ins, "f32", "f32", "f32")
+    check_all(outs, oracle.allreduce(cols, "f32", "f32"), "f32", "special f32")
+    codes = [np.arange(256, dtype=np.uint8)[np.random.default_rng(s).permutation(256)]
+             for s in range(n)]
+    ins = [torch.from_numpy(c).cuda() for c in codes]
+    for acc in ("f32", "f16", "fp8"):
+        for tout in ("fp8", "f16", "f32"):
+            outs = run(ins, "fp8", acc, tout)
+            check_all(outs, oracle.allreduce(codes, "fp8", acc, tout), tout,
+                      "special fp8 %s/%s" % (acc, tout))
+
+
+def test_rank_order_pin():
+    """x_0 = 1, x_1..7 = 2^-24 in f32: only the sequential rank order gives 1.0."""
+    announce("rsag order pin")
+    count = 4096
+    ins = [torch.full((count,), 1.0, device="cuda")] + \
+          [torch.full((count,), 2.0 ** -24, device="cuda") for _ in range(7)]
+    outs = run(ins, "f32", "f32", "f32")
+    for o in outs:
+        assert torch.all(o == 1.0).item()
+
+
+def test_graph_replays_match_eager():
+    n, count, t = 8, 1 << 20, "f16"
+    announce("rsag graph")
+    ins = inputs_for(t, n, count, seed0=21)
+    eager = run(ins, t, "f32", t)
+    outs = [empty(t, count, 0) for _ in range(n)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            assert mrr.mrr_allreduce_rsag(ins, outs, count, t, n, stream=s) == mrr.MRR_OK
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(n):
+            assert torch.equal(outs[k], eager[k]), "replay %d out %d" % (rep, k)
+
+
+# ---------------------------------------------------------------------------
+# Full sizes, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+def sample_indices(count, n, vw, rng, k=1 << 18):
+    per = -(-count // n)
+    chunk = -(-per // vw) * vw
+    edges = []
+    for r in range(n + 1):
+        for d in (-2, -1, 0, 1):
+            i = r * chunk + d
+            if 0 <= i < count:
+                edges.append(i)
+    idx = np.concatenate([rng.integers(0, count, k), np.array(edges + [count - 1], np.int64)])
+    return torch.from_numpy(np.unique(idx)).cuda()
+
+
+def test_full_size_eight_ranks_64mib_f16():
+    """8 ranks x 64 MiB of f16 ~N(0,1): whole output 0 against the oracle, and
+    all eight outputs identical."""
+    n, count, t = 8, 64 * (1 << 20) // 2, "f16"
+    announce("rsag 8x64MiB f16 full")
+    ins = inputs_for(t, n, count, seed0=0)
+    outs = [empty(t, count) for _ in range(n)]
+    assert mrr.mrr_allreduce_rsag(ins, outs, count, t, n) == mrr.MRR_OK
+    torch.cuda.synchronize()
+    want = oracle.allreduce([bits(x) for x in ins], t, "f32")
+    assert_bits_equal(bits(outs[0]), want, t, "8x64MiB out[0]")
+    for k in range(1, n):
+        assert torch.equal(outs[k].view(torch.int16), outs[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("tout", ["f16", "fp8"])
+def test_full_size_fp8_eight_ranks_32mib(tout):
+    n, count = 8, 32 * (1 << 20)
+    announce("rsag 8x32MiB fp8 ->", tout)
+    ins = inputs_for("fp8", n, count, seed0=100)
+    outs = [empty(tout, count) for _ in range(n)]
+    st = mrr.mrr_allreduce_rsag_ex(ins, outs, count, "fp8", "f32", tout, n, -1)
+    assert st == mrr.MRR_OK
+    torch.cuda.synchronize()
+    want = oracle.allreduce([bits(x) for x in ins], "fp8", "f32", tout)
+    assert_bits_equal(bits(outs[0]), want, tout, "fp8 out[0]")
+    for k in range(1, n):
+        assert torch.equal(outs[k].view(torch.uint8), outs[0].view(torch.uint8))
+
+
+@pytest.mark.parametrize("n", RANKS)
+def test_rank_sweep_256mib_bf16_sampled(n):
+    """N x 256 MiB of bf16 ~N(0,1) (inputs drawn on the device): sampled
+    outputs against the oracle, chunk edges included, all outputs identical."""
+    count, t = 256 * (1 << 20) // 2, "bf16"
+    announce("rsag sweep 256MiB bf16 n=%d" % n)
+    ins = inputs_for(t, n, count, seed0=1000, device="cuda")
+    outs = [empty(t, count) for _ in range(n)]
+    assert mrr.mrr_allreduce_rsag(ins, outs, count, t, n) == mrr.MRR_OK
+    torch.cuda.synchronize()
+    idx = sample_indices(count, n, VW[t], np.random.default_rng(n))
+    sub_in = [bits(x[idx]) for x in ins]
+    want = oracle.allreduce(sub_in, t, "f32")
+    for k in range(n):
+        assert_bits_equal(bits(outs[k][idx]), want, t, "n=%d out[%d]" % (n, k))
+        if k:
+            assert torch.equal(outs[k].view(torch.int16), outs[0].view(torch.int16))
+    del ins, outs
+    torch.cuda.empty_cache()
