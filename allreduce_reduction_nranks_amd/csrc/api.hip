@@ -130,7 +130,8 @@ mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs
     return refuse(MRR_EUNSUPPORTED, fn, "type combination");
   if (count == 0) return MRR_OK;
   const size_t ein = tsize(tin), eout = tsize(tout);
-  if (count > (SIZE_MAX / 4) / eout) return refuse(MRR_EINVAL, fn, "count too large");
+  if (count > ((uint64_t)1 << 40) / (ein > eout ? ein : eout))
+    return refuse(MRR_EINVAL, fn, "count too large for one call (over 1 TiB per buffer)");
   bool vec = true;
   for (int r = 0; r < nranks; ++r) {
     if (!inputs[r] || !outputs[r]) return refuse(MRR_EINVAL, fn, "null buffer");

@@ -22,9 +22,9 @@ struct RsagArgs {
   uint64_t total_vecs;    // whole 16-byte input vectors in [0, count)
   uint64_t tail_begin;    // first element not covered by a whole vector
   uint32_t tail_count;    // elements in the tail handled by this launch (0..15)
-  uint32_t first_chunk;   // chunk handled by workgroup 0
+  uint32_t first_chunk;   // first chunk of the launch
   uint32_t tiles_per_chunk;
-  uint32_t pad;
+  uint32_t launch_tiles;  // tiles of all chunks in the launch
 };
 
 // Element-wise kernel arguments (pointers not 16-byte aligned).

@@ -8,30 +8,51 @@
 //
 // MI355X mapping.  All N rank buffers live in this GPU's HBM, so one launch
 // performs every rank's share (or one chosen rank's share).  The work is
-// HBM-bound (N*S bytes read, N*S written, ~N VALU adds per element), so the
-// design is about keeping enough 16-byte loads in flight:
-//   - workgroup g handles tile (g % tiles_per_chunk) of chunk
-//     first_chunk + g / tiles_per_chunk: the reduce-scatter partition, chunk
-//     by chunk;
-//   - each lane owns U 16-byte vectors of the tile (lane-contiguous, so every
-//     wave-level load and store instruction covers 1 KiB of one buffer);
-//   - all U*N loads are issued before any add (non-temporal: the data is
-//     touched once), then each vector is accumulated in rank order 0..N-1,
-//     narrowed once, and stored to all N outputs (the all-gather) with
-//     non-temporal 16-byte stores.
+// HBM-bound (N*S bytes read, N*S written, ~N VALU adds per element); what
+// decides the bandwidth is how many bytes are in flight and how the 2N
+// same-offset streams hit the DRAM banks:
+//   - the reduce-scatter partition is kept at tile granularity: tile i of
+//     the launch is tile (i % tiles_per_chunk) of chunk
+//     first_chunk + i / tiles_per_chunk, and no tile straddles two chunks;
+//   - a persistent grid of single-wave (64-lane) workgroups strides over the
+//     tiles; each lane owns U 16-byte vectors of a tile (lane-contiguous, so
+//     every load/store instruction covers 1 KiB of one buffer), issues all
+//     U*N loads (non-temporal: the data is touched once), accumulates each
+//     vector in rank order 0..N-1, narrows once and stores the result to all
+//     N outputs (the all-gather) with non-temporal 16-byte stores;
+//   - few waves per CU stream best (one to eight single-wave workgroups per
+//     CU, see the launch-shape table below): more loads in flight thrash DRAM
+//     rows across the 2N same-offset buffers, fewer leave HBM latency
+//     exposed.
 // No __restrict__: an output may be its own rank's input (in place); a lane
 // reads every element it writes before writing it.
+#include <stdlib.h>
+
 #include "mrr_device.hpp"
 #include "mrr_internal.hpp"
 
 namespace mrr {
 
-constexpr int kRsagThreads = 256;
+constexpr int kRsagThreads = 64;  // one wave per workgroup
 
-// 16-byte vectors per lane per tile: enough independent loads in flight at
-// small N, bounded register use at large N.
+// Launch shape, from a sweep of (vectors per lane U) x (workgroups per CU)
+// of this kernel on MI355X with rank buffers allocated one after another
+// (64 MiB and 256 MiB per rank).  Streaming bandwidth is bumpy in both knobs
+// -- the 2N same-offset streams interact with the DRAM channel and bank
+// mapping -- so each entry is the setting that stayed near the best across
+// buffer sizes rather than a formula.
+//   16-bit and 32-bit inputs: N=2 U=8 x2, N=4 U=4 x4, N=8 U=1 x6,
+//                             N=16 U=2 x2, N=32 U=1 x8 (workgroups per CU)
+//   FP8 inputs (16 elements and accumulators per vector, ALU-heavier):
+//                             U=4 for N=2, else 1; 4 workgroups per CU for
+//                             wider outputs, 16 for FP8 outputs.
 constexpr int rsag_unroll(int n, int tin) {
-  return tin == kFP8 ? (n <= 4 ? 2 : 1) : (n <= 2 ? 4 : (n <= 8 ? 2 : 1));
+  if (tin == kFP8) return n == 2 ? 4 : 1;
+  return n == 2 ? 8 : n == 4 ? 4 : n == 16 ? 2 : 1;
+}
+constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
+  if (tin == kFP8) return tout == kFP8 ? 16 : 4;
+  return n == 2 ? 2 : n == 4 ? 4 : n == 8 ? 6 : n == 16 ? 2 : 8;
 }
 // Ranks whose vectors are loaded together before they are added: all of them
 // up to 16 ranks; groups of 16 (8 with an FP8 accumulator, whose per-element
@@ -102,23 +123,24 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
 template <int N, int In, int Acc, int Out, int U>
 __global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a) {
   constexpr int G = rsag_group(N, Acc);
-  const uint32_t chunk_rel = blockIdx.x / a.tiles_per_chunk;
-  const uint32_t tile = blockIdx.x - chunk_rel * a.tiles_per_chunk;
-  const uint64_t v_lo = (uint64_t)(a.first_chunk + chunk_rel) * a.chunk_vecs;
-  const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
-  const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
-
-  if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
-    reduce_store<N, In, Acc, Out, U, G>(a, v0);
-  } else {
+  for (uint32_t i = blockIdx.x; i < a.launch_tiles; i += gridDim.x) {
+    const uint32_t chunk_rel = i / a.tiles_per_chunk;
+    const uint32_t tile = i - chunk_rel * a.tiles_per_chunk;
+    const uint64_t v_lo = (uint64_t)(a.first_chunk + chunk_rel) * a.chunk_vecs;
+    const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
+    const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
+    if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
+      reduce_store<N, In, Acc, Out, U, G>(a, v0);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
-      if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G>(a, v);
+      for (int u = 0; u < U; ++u) {
+        const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
+        if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G>(a, v);
+      }
     }
   }
-  // Elements past the last whole vector (count % VW of them) go to the last
-  // workgroup, one per lane.
+  // Elements past the last whole vector (count % VW of them, fewer than one
+  // wave) go to the last workgroup, one per lane.
   if (a.tail_count != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < a.tail_count)
     reduce_elem<In, Acc, Out>(a.in, a.out, N, a.tail_begin + threadIdx.x);
 }
@@ -204,7 +226,18 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
       nchunks = 1;
       a.tail_count = tail_chunk == (uint64_t)p.rank ? tail : 0;
     }
-    const dim3 grid(nchunks * a.tiles_per_chunk);
+    a.launch_tiles = nchunks * a.tiles_per_chunk;
+    // Persistent grid: wg_per_cu workgroups per CU (MRR_RSAG_WPC overrides).
+    int wpc = rsag_wg_per_cu(n, p.tin, p.tout);
+    static const int wpc_env = [] {
+      const char* v = getenv("MRR_RSAG_WPC");
+      return v ? atoi(v) : 0;
+    }();
+    if (wpc_env > 0) wpc = wpc_env;
+    uint64_t blocks = (uint64_t)device_cu_count(-1) * (uint64_t)wpc;
+    if (blocks == 0) blocks = 1024;
+    if (blocks > a.launch_tiles) blocks = a.launch_tiles;
+    const dim3 grid((uint32_t)blocks);
 #define MRR_DISPATCH(I, A, O) \
   if (p.tin == I && p.tacc == A && p.tout == O) launch_vec_typed<I, A, O>(n, grid, a, stream);
     MRR_RSAG_TRIPLES(MRR_DISPATCH)
