@@ -157,6 +157,84 @@ template <int T> __device__ __forceinline__ void store_elem(void* p, uint64_t i,
 }
 
 // ---------------------------------------------------------------------------
+// FP8 E4M3B15 through the gfx950 OCP FP8 converts.
+//
+// The hardware converts between f32 and OCP FP8 E4M3 (bias 7) exactly
+// (decode) and with round-to-nearest-even (encode), subnormals included.  For
+// exponent fields 0..14 an E4M3B15 code has the bit layout of the E4M3 code
+// of 2^8 times its value, subnormals included, so
+//   decode_b15(c) = decode_e4m3(c) * 2^-8       (one scaled convert)
+//   encode_b15(x) = encode_e4m3(clamp(x * 2^8, -240, 240))
+// where 240 = 0.9375 * 2^8 is the largest E4M3B15 value, so the clamp is the
+// saturation.  Exponent field 15 differs (inf / NaN here, finite or NaN in
+// E4M3): codes with it are detected per 16-byte vector and fixed up, and
+// values derived from them take the exact bit-arithmetic path above.
+// ---------------------------------------------------------------------------
+// True when any byte of the vector has exponent field 15.
+__device__ __forceinline__ bool fp8_any_e15(const u32x4 v) {
+  uint32_t hit = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = (v[j] & 0x78787878u) ^ 0x78787878u;  // zero byte <=> e == 15
+    hit |= (t - 0x01010101u) & ~t & 0x80808080u;
+  }
+  return hit != 0;
+}
+
+// 16 codes -> 16 f32 values (exact for exponent fields <= 14).
+__device__ __forceinline__ void decode16_fp8_hw(const u32x4 v, float* x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = v[j];
+    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 0x1p-8f, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 0x1p-8f, true);
+    x[4 * j] = lo.x;
+    x[4 * j + 1] = lo.y;
+    x[4 * j + 2] = hi.x;
+    x[4 * j + 3] = hi.y;
+  }
+}
+
+// Replaces the values of exponent-15 codes by inf (mantissa 0) or NaN.
+__device__ __forceinline__ void fix_fp8_e15(const u32x4 v, float* x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t c = (v[j] >> (8 * b)) & 0xFFu;
+      if ((c & 0x78u) == 0x78u) x[4 * j + b] = fp8_to_f32(c);
+    }
+  }
+}
+
+// Finite f32 -> E4M3B15 bits of a pair, packed into the low (HI = false) or
+// high (HI = true) 16 bits of `old`; the other half of `old` is kept.
+template <bool HI>
+__device__ __forceinline__ uint32_t encode2_fp8_hw(float a, float b, uint32_t old) {
+  const float ya = __builtin_amdgcn_fmed3f(a * 256.0f, -240.0f, 240.0f);
+  const float yb = __builtin_amdgcn_fmed3f(b * 256.0f, -240.0f, 240.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, (int)old, HI);
+}
+
+// 16 finite f32 values -> one 16-byte vector of E4M3B15 codes.
+__device__ __forceinline__ u32x4 encode16_fp8_hw(const float* x) {
+  u32x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = encode2_fp8_hw<false>(x[4 * j], x[4 * j + 1], 0u);
+    v[j] = encode2_fp8_hw<true>(x[4 * j + 2], x[4 * j + 3], w);
+  }
+  return v;
+}
+
+// Rounds a finite f32 sum to the E4M3B15 grid (native FP8 accumulation).
+__device__ __forceinline__ float round_fp8_hw(float s) {
+  const uint32_t c = encode2_fp8_hw<false>(s, s, 0u);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 0x1p-8f, false);
+  return d.x;
+}
+
+// ---------------------------------------------------------------------------
 // 16-byte vector decode / encode.  An input vector holds VW = 16 / size(In)
 // elements; its output holds VW * size(Out) bytes = OV 16-byte vectors.
 // ---------------------------------------------------------------------------

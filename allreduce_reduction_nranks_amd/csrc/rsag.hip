@@ -43,22 +43,23 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup
 // buffer sizes rather than a formula.
 //   16-bit and 32-bit inputs: N=2 U=8 x2, N=4 U=4 x4, N=8 U=1 x6,
 //                             N=16 U=2 x2, N=32 U=1 x8 (workgroups per CU)
-//   FP8 inputs (16 elements and accumulators per vector, ALU-heavier):
-//                             U=4 for N=2, else 1; 4 workgroups per CU for
-//                             wider outputs, 16 for FP8 outputs.
+//   FP8 inputs (16 elements and accumulators per vector): U=4 for N=2,
+//                             else 1; 4 workgroups per CU for FP8 outputs,
+//                             2 for the wider (write-heavier) outputs.
 constexpr int rsag_unroll(int n, int tin) {
   if (tin == kFP8) return n == 2 ? 4 : 1;
   return n == 2 ? 8 : n == 4 ? 4 : n == 16 ? 2 : 1;
 }
 constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
-  if (tin == kFP8) return tout == kFP8 ? 16 : 4;
+  if (tin == kFP8) return tout == kFP8 ? 4 : 2;
   return n == 2 ? 2 : n == 4 ? 4 : n == 8 ? 6 : n == 16 ? 2 : 8;
 }
 // Ranks whose vectors are loaded together before they are added: all of them
-// up to 16 ranks; groups of 16 (8 with an FP8 accumulator, whose per-element
-// rounding makes the unrolled body large) above that.
-constexpr int rsag_group(int n, int tacc) {
-  return tacc == kFP8 ? (n < 8 ? n : 8) : (n < 16 ? n : 16);
+// up to 16 ranks; groups of 16 above that, and groups of 8 for FP8 inputs or
+// an FP8 accumulator (16 values per vector and two decode paths make the
+// unrolled body large).
+constexpr int rsag_group(int n, int tin, int tacc) {
+  return (tin == kFP8 || tacc == kFP8) ? (n < 8 ? n : 8) : (n < 16 ? n : 16);
 }
 
 template <int In, int Acc, int Out>
@@ -72,9 +73,14 @@ __device__ __forceinline__ void reduce_elem(const void* const* in, void* const* 
 // Reduces UU vector positions v0 + u * kRsagThreads (u < UU) over the N ranks
 // and stores each result to all N outputs.  The first partial sum is x_0
 // rounded to the accumulator type (the identity except for an FP8
-// accumulator, which saturates an infinite x_0 like any later sum).  Ranks are taken in groups of G:
-// the group's UU * G loads are all issued before the first add of the group,
-// then the adds run in rank order.
+// accumulator, which saturates an infinite x_0 like any later sum).  Ranks
+// are taken in groups of G: the group's UU * G loads are all issued before
+// the first add of the group, then the adds run in rank order.
+//
+// FP8 inputs decode through the hardware E4M3 converts; a lane whose vectors
+// hold an exponent-15 code (inf / NaN) marks that position `special`, fixes
+// those values, and rounds / encodes that position with the exact bit
+// arithmetic instead of the converts, which are only exact for finite data.
 template <int N, int In, int Acc, int Out, int UU, int G>
 __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
   constexpr int VW = Vec<In>::VW;
@@ -82,6 +88,9 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
   constexpr int OW = Vec<Out>::VW;                  // elements per output vector
   static_assert(N % G == 0, "rank group must divide N");
   float acc[UU][VW];
+  bool special[UU];
+#pragma unroll
+  for (int u = 0; u < UU; ++u) special[u] = false;
 #pragma unroll(N / G <= 2 ? N / G : 1)
   for (int g = 0; g < N; g += G) {
     u32x4 raw[UU][G];
@@ -95,13 +104,20 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
 #pragma unroll
       for (int r = 0; r < G; ++r) {
         float x[VW];
-        decode16<In>(raw[u][r], x);
-        if (g + r == 0) {
-#pragma unroll
-          for (int j = 0; j < VW; ++j) acc[u][j] = round_acc<Acc>(x[j]);
+        if constexpr (In == kFP8) {
+          decode16_fp8_hw(raw[u][r], x);
+          if (fp8_any_e15(raw[u][r])) {
+            fix_fp8_e15(raw[u][r], x);
+            special[u] = true;
+          }
         } else {
+          decode16<In>(raw[u][r], x);
+        }
 #pragma unroll
-          for (int j = 0; j < VW; ++j) acc[u][j] = round_acc<Acc>(acc[u][j] + x[j]);
+        for (int j = 0; j < VW; ++j) {
+          const float s = g + r == 0 ? x[j] : acc[u][j] + x[j];
+          if constexpr (Acc == kFP8) acc[u][j] = special[u] ? round_acc<kFP8>(s) : round_fp8_hw(s);
+          else acc[u][j] = round_acc<Acc>(s);
         }
       }
     }
@@ -111,7 +127,10 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
     const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
     u32x4 o[OV];
 #pragma unroll
-    for (int q = 0; q < OV; ++q) o[q] = encode16<Out>(acc[u] + q * OW);
+    for (int q = 0; q < OV; ++q) {
+      if constexpr (Out == kFP8) o[q] = special[u] ? encode16<kFP8>(acc[u] + q * OW) : encode16_fp8_hw(acc[u] + q * OW);
+      else o[q] = encode16<Out>(acc[u] + q * OW);
+    }
 #pragma unroll
     for (int k = 0; k < N; ++k) {
 #pragma unroll
@@ -122,7 +141,7 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
 
 template <int N, int In, int Acc, int Out, int U>
 __global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a) {
-  constexpr int G = rsag_group(N, Acc);
+  constexpr int G = rsag_group(N, In, Acc);
   for (uint32_t i = blockIdx.x; i < a.launch_tiles; i += gridDim.x) {
     const uint32_t chunk_rel = i / a.tiles_per_chunk;
     const uint32_t tile = i - chunk_rel * a.tiles_per_chunk;
