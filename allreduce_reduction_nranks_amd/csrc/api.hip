@@ -175,8 +175,8 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   const int tacc = accum == MRR_AUTO ? t : (int)accum;
   if (!tsize(t) || !packet_supported(nranks, t, tacc))
     return refuse(MRR_EUNSUPPORTED, fn, "type combination");
-  if (threads != 0 && (threads < 64 || threads > 1024 || threads % 64 != 0))
-    return refuse(MRR_EINVAL, fn, "threads must be a multiple of 64 in [64, 1024]");
+  if (threads != 0 && (threads < 64 || threads > packet_max_threads() || threads % 64 != 0))
+    return refuse(MRR_EINVAL, fn, "threads must be a multiple of 64 in [64, 512]");
   if (blocks_per_rank < 0 || blocks_per_rank > MRR_PKT_FLAG_SLOTS)
     return refuse(MRR_EINVAL, fn, "blocks_per_rank outside [1, MRR_PKT_FLAG_SLOTS]");
   if (!aligned(scratch, 8) || !aligned(flags, 4)) return refuse(MRR_EALIGN, fn, "scratch/flags");
@@ -204,7 +204,7 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   }
 
   const uint64_t npkt = (nbytes + 3) / 4;
-  const int T = threads ? threads : 512;
+  const int T = threads ? threads : 64;
   int B = blocks_per_rank;
   // Geometry needs the device: how many workgroups fit at once.
   const void* kernel = packet_allpair_kernel(nranks, t, tacc);
@@ -212,11 +212,13 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   if (resident <= 0) return hip_status(hipErrorInvalidDevice, fn);
   const int max_b = resident / nranks;
   if (B == 0) {
-    // About 4 packets per lane, as many blocks as fit, never more than slots.
-    const uint64_t want = (npkt + (uint64_t)T * 4 - 1) / ((uint64_t)T * 4);
-    B = (int)(want < 1 ? 1 : want);
+    // One poll round per lane when the GPU can hold that many workgroups:
+    // every round costs a memory round trip, and more workgroups spread the
+    // sends and polls over more CUs.
+    const uint64_t per_block = (uint64_t)T * packet_batch(nranks);
+    const uint64_t want = (npkt + per_block - 1) / per_block;
+    B = (int)(want < 1 ? 1 : (want > (uint64_t)MRR_PKT_FLAG_SLOTS ? MRR_PKT_FLAG_SLOTS : want));
     if (B > max_b) B = max_b;
-    if (B > MRR_PKT_FLAG_SLOTS) B = MRR_PKT_FLAG_SLOTS;
   }
   if (B < 1 || B > max_b)
     return refuse(MRR_EINVAL, fn, "nranks * blocks_per_rank workgroups do not fit on the GPU at once");

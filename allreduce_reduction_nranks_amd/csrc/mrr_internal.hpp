@@ -71,6 +71,10 @@ struct PacketReduceArgs {
 };
 
 bool packet_supported(int nranks, int t, int tacc);
+// Packets per lane that one poll round of the allpair / reduce kernels covers.
+int packet_batch(int nranks);
+// Largest workgroup size the allpair kernel is built for.
+int packet_max_threads();
 // Pointer to the allpair kernel for (nranks, t, tacc), used for occupancy.
 const void* packet_allpair_kernel(int nranks, int t, int tacc);
 hipError_t launch_packet_allpair(const PacketArgs& a, int nranks, int t, int tacc, int threads,

@@ -82,8 +82,62 @@ __device__ __forceinline__ void report_timeout(uint32_t* dev_err) {
   if (dev_err) atomicCAS(dev_err, 0u, (uint32_t)MRR_ETIMEDOUT);
 }
 
+// Packets per lane handled in one poll round (all P x (N - 1) loads in flight
+// together).  Measured on MI355X: one packet per lane and more workgroups
+// beats batching, which costs registers and therefore co-resident
+// workgroups; the latency of a call is set by how many CUs take part.
+constexpr int pkt_batch(int) { return 1; }
+// Largest workgroup of the allpair kernel (bounds its registers at 256).
+constexpr int kPktMaxThreads = 512;
+int packet_max_threads() { return kPktMaxThreads; }
+
+template <int N>
+__device__ __forceinline__ uint32_t peer_mask(uint32_t self) {
+  const uint32_t all = N == 32 ? 0xFFFFFFFFu : ((1u << N) - 1u);
+  return self < (uint32_t)N ? all & ~(1u << self) : all;
+}
+
+// Source s of packet k lives at addr(s) + k.
+struct StridedSources {  // one scratch, sources `stride` packets apart
+  const uint64_t* base;
+  uint64_t stride;
+  __device__ __forceinline__ const uint64_t* operator()(int s) const { return base + (uint64_t)s * stride; }
+};
+struct ListedSources {  // one pointer per source
+  const uint64_t* const* ptr;
+  __device__ __forceinline__ const uint64_t* operator()(int s) const { return ptr[s]; }
+};
+
+// Waits until every pending packet (bit s of pending[p]: source s of packet
+// kp[p]) carries `flag`, filling w[p][s] with the payloads.  Wavefront-uniform:
+// all lanes leave together.  Returns false after max_spins rounds (0 = none).
+template <int N, int P, typename Src>
+__device__ __forceinline__ bool poll_batch(const Src& src, const uint64_t* kp, uint32_t* pending,
+                                           uint32_t (*w)[N], uint32_t flag, uint32_t max_spins) {
+  uint32_t spins = 0;
+  while (true) {
+    uint32_t left = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        if (pending[p] & (1u << s)) {
+          const uint64_t pk = ld_pkt(src(s) + kp[p]);
+          w[p][s] = (uint32_t)pk;
+          if ((uint32_t)(pk >> 32) == flag) pending[p] &= ~(1u << s);
+        }
+      }
+      left |= pending[p];
+    }
+    if (__all(left == 0u)) return true;
+    if (max_spins != 0u && ++spins >= max_spins) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 template <int N, int T, int Acc>
-__global__ void __launch_bounds__(1024) packet_allpair_k(const PacketArgs a) {
+__global__ void __launch_bounds__(kPktMaxThreads) packet_allpair_k(const PacketArgs a) {
+  constexpr int P = pkt_batch(N);
   const uint32_t d = blockIdx.x % N;
   const uint32_t b = blockIdx.x / N;
   uint32_t* const my_flags = a.flags + (uint64_t)d * kFlagSlots;
@@ -102,38 +156,30 @@ __global__ void __launch_bounds__(1024) packet_allpair_k(const PacketArgs a) {
       if ((uint32_t)p != d) st_pkt(a.scratch + ((uint64_t)p * N + d) * a.npkt + k, pkt);
   }
 
-  // Receive, reduce and write back, a wavefront-uniform loop over the slice.
-  const uint64_t* const inbox = a.scratch + (uint64_t)d * N * a.npkt;
-  bool timed_out = false;
-  for (uint64_t kb = k_lo; kb < k_hi && !timed_out; kb += blockDim.x) {
-    const uint64_t k = kb + threadIdx.x;
-    const bool active = k < k_hi;
-    uint32_t w[N];
-    uint32_t pending = 0;
+  // Receive, reduce and write back, in wavefront-uniform batches of P
+  // packets per lane.
+  const StridedSources inbox{a.scratch + (uint64_t)d * N * a.npkt, a.npkt};
+  const uint64_t step = (uint64_t)blockDim.x * P;
+  for (uint64_t kb = k_lo; kb < k_hi; kb += step) {
+    uint64_t kp[P];
+    uint32_t pending[P];
+    uint32_t w[P][N];
 #pragma unroll
-    for (int s = 0; s < N; ++s)
-      if (active && (uint32_t)s != d) pending |= 1u << s;
-    uint32_t spins = 0;
-    while (true) {
-#pragma unroll
-      for (int s = 0; s < N; ++s) {
-        if (pending & (1u << s)) {
-          const uint64_t pk = ld_pkt(inbox + (uint64_t)s * a.npkt + k);
-          w[s] = (uint32_t)pk;
-          if ((uint32_t)(pk >> 32) == F) pending &= ~(1u << s);
-        }
-      }
-      if (__all(pending == 0u)) break;
-      if (a.max_spins != 0u && ++spins >= a.max_spins) {
-        report_timeout(a.dev_err);
-        timed_out = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+    for (int p = 0; p < P; ++p) {
+      kp[p] = kb + (uint64_t)p * blockDim.x + threadIdx.x;
+      pending[p] = kp[p] < k_hi ? peer_mask<N>(d) : 0u;
     }
-    if (timed_out || !active) continue;
-    const uint32_t own = load_word(src, a.nbytes, k);
-    store_word(a.out[d], a.nbytes, k, reduce_word<N, T, Acc>(w, d, own));
+    if (!poll_batch<N, P>(inbox, kp, pending, w, F, a.max_spins)) {
+      report_timeout(a.dev_err);
+      break;
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (kp[p] < k_hi) {
+        const uint32_t own = load_word(src, a.nbytes, kp[p]);
+        store_word(a.out[d], a.nbytes, kp[p], reduce_word<N, T, Acc>(w[p], d, own));
+      }
+    }
   }
 
   // Flag update: every slot j of rank d with j % B == b, by a thread loop so
@@ -147,36 +193,25 @@ __global__ void __launch_bounds__(1024) packet_allpair_k(const PacketArgs a) {
 // Receive step alone: packets from N producers outside the launch.
 template <int N, int T, int Acc>
 __global__ void __launch_bounds__(256) packet_reduce_k(const PacketReduceArgs a) {
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  bool timed_out = false;
-  for (uint64_t kb = (uint64_t)blockIdx.x * blockDim.x; kb < a.npkts && !timed_out; kb += stride) {
-    const uint64_t k = kb + threadIdx.x;
-    const bool active = k < a.npkts;
-    uint32_t w[N];
-    uint32_t pending = 0;
+  constexpr int P = pkt_batch(N);
+  const uint64_t step = (uint64_t)gridDim.x * blockDim.x * P;
+  for (uint64_t kb = (uint64_t)blockIdx.x * blockDim.x * P; kb < a.npkts; kb += step) {
+    uint64_t kp[P];
+    uint32_t pending[P];
+    uint32_t w[P][N];
 #pragma unroll
-    for (int s = 0; s < N; ++s)
-      if (active) pending |= 1u << s;
-    uint32_t spins = 0;
-    while (true) {
-#pragma unroll
-      for (int s = 0; s < N; ++s) {
-        if (pending & (1u << s)) {
-          const uint64_t pk = ld_pkt(a.in[s] + k);
-          w[s] = (uint32_t)pk;
-          if ((uint32_t)(pk >> 32) == a.flag_in) pending &= ~(1u << s);
-        }
-      }
-      if (__all(pending == 0u)) break;
-      if (a.max_spins != 0u && ++spins >= a.max_spins) {
-        report_timeout(a.dev_err);
-        timed_out = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+    for (int p = 0; p < P; ++p) {
+      kp[p] = kb + (uint64_t)p * blockDim.x + threadIdx.x;
+      pending[p] = kp[p] < a.npkts ? peer_mask<N>((uint32_t)N) : 0u;
     }
-    if (timed_out || !active) continue;
-    st_pkt(a.out + k, make_pkt(reduce_word<N, T, Acc>(w, (uint32_t)N, 0u), a.flag_out));
+    if (!poll_batch<N, P>(ListedSources{a.in}, kp, pending, w, a.flag_in, a.max_spins)) {
+      report_timeout(a.dev_err);
+      break;
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (kp[p] < a.npkts)
+        st_pkt(a.out + kp[p], make_pkt(reduce_word<N, T, Acc>(w[p], (uint32_t)N, 0u), a.flag_out));
   }
 }
 
@@ -238,9 +273,12 @@ hipError_t launch_packet_allpair(const PacketArgs& a, int nranks, int t, int tac
   return hipErrorInvalidValue;
 }
 
+int packet_batch(int nranks) { return pkt_batch(nranks); }
+
 hipError_t launch_packet_reduce(const PacketReduceArgs& a, int nranks, int t, int tacc,
                                 hipStream_t stream) {
-  uint64_t blocks = (a.npkts + 255) / 256;
+  const uint64_t per_block = 256ull * pkt_batch(nranks);
+  uint64_t blocks = (a.npkts + per_block - 1) / per_block;
   if (blocks > 4096) blocks = 4096;
   const dim3 grid((uint32_t)blocks), block(256);
 #define MRR_K(N, T, A)                                                               \

@@ -160,7 +160,7 @@ mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs
  *           bound.  Read *dev_err after synchronising the stream.
  * blocks_per_rank / threads (_ex only): B and the workgroup size; 0 = auto.
  *           B must be in [1, MRR_PKT_FLAG_SLOTS]; threads a multiple of 64 in
- *           [64, 1024]; nranks * B workgroups must fit on the GPU at once
+ *           [64, 512]; nranks * B workgroups must fit on the GPU at once
  *           (every workgroup waits for its peers), else MRR_EINVAL.
  * Calls that overlap in time on the same scratch or flags race; calls on one
  * stream never overlap.

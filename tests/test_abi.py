@@ -139,6 +139,7 @@ def test_packet_argument_checks(lib):
     assert packet(sbytes=mrr.mrr_packet_scratch_bytes(4096, "f16", 8) - 8) == mrr.MRR_ESCRATCH
     assert packet(threads=100) == mrr.MRR_EINVAL
     assert packet(threads=2048) == mrr.MRR_EINVAL
+    assert packet(threads=1024) == mrr.MRR_EINVAL  # the allpair kernel is built for <= 512
     assert packet(blocks=1025) == mrr.MRR_EINVAL
     assert packet(scratch=fake(200, off=4)) == mrr.MRR_EALIGN
     ins = [fake(r) for r in range(8)]

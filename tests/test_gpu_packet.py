@@ -99,7 +99,7 @@ def test_geometry_changes_between_calls():
     n, t, count = 8, "f16", 40000
     st = PacketState(n, count, t)
     outs = [empty(t, count) for _ in range(n)]
-    geoms = [(1, 64), (3, 128), (64, 256), (7, 1024), (0, 0), (200, 64), (1, 1024), (16, 512)]
+    geoms = [(1, 64), (3, 128), (64, 256), (7, 512), (0, 0), (200, 64), (1, 512), (16, 448)]
     for it, (b, th) in enumerate(geoms, start=1):
         announce("packet geometry", b, th)
         ins = inputs_for(t, n, count, seed0=50 + it, kind="uniform")
