@@ -68,6 +68,7 @@ def load_library() -> ctypes.CDLL:
             "mrr_fp8b15_to_f32": ([vp, vp, sz, vp], i),
             "mrr_f16_to_fp8b15": ([vp, vp, sz, vp], i),
             "mrr_f32_to_fp8b15": ([vp, vp, sz, vp], i),
+            "mrr_rank_buffer_pitch": ([sz, i], sz),
             "mrr_status_string": ([i], ctypes.c_char_p),
             "mrr_version": ([], i),
         }
@@ -122,6 +123,26 @@ def mrr_status_string(status: int) -> str:
 
 def mrr_version() -> int:
     return load_library().mrr_version()
+
+
+def mrr_rank_buffer_pitch(bytes_per_rank: int, nranks: int) -> int:
+    return load_library().mrr_rank_buffer_pitch(bytes_per_rank, nranks)
+
+
+def alloc_rank_buffers(nranks: int, count: int, dtype, device=None):
+    """N rank buffers of `count` elements carved from one device allocation
+    at mrr_rank_buffer_pitch() spacing.  Returns (pool, [views])."""
+    import torch
+    tdt = dtype if isinstance(dtype, torch.dtype) else \
+        {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+         "fp8": torch.uint8, "fp8_e4m3b15": torch.uint8}[dtype]
+    esize = torch.empty((), dtype=tdt).element_size()
+    nbytes = count * esize
+    pitch = mrr_rank_buffer_pitch(nbytes, nranks)
+    pool = torch.empty(max(1, nranks * pitch), dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+    views = [pool[r * pitch: r * pitch + nbytes].view(tdt) for r in range(nranks)]
+    return pool, views
 
 
 def mrr_allreduce_rsag(inputs, outputs, count, dtype, nranks, stream=None) -> int:

@@ -116,6 +116,13 @@ const char* mrr_status_string(mrr_status s) {
 
 int mrr_version(void) { return 10000; }
 
+size_t mrr_rank_buffer_pitch(size_t bytes_per_rank, int nranks) {
+  if (bytes_per_rank == 0 || nranks < 1) return 0;
+  const size_t page = 4096;
+  const size_t stagger = nranks >= 16 ? 2048 : 4096;
+  return (bytes_per_rank + page - 1) / page * page + stagger;
+}
+
 mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs, size_t count,
                                  mrr_dtype in, mrr_dtype accum, mrr_dtype out, int nranks,
                                  int rank, void* stream) {

@@ -167,46 +167,9 @@ template <int T> __device__ __forceinline__ void store_elem(void* p, uint64_t i,
 //   encode_b15(x) = encode_e4m3(clamp(x * 2^8, -240, 240))
 // where 240 = 0.9375 * 2^8 is the largest E4M3B15 value, so the clamp is the
 // saturation.  Exponent field 15 differs (inf / NaN here, finite or NaN in
-// E4M3): codes with it are detected per 16-byte vector and fixed up, and
-// values derived from them take the exact bit-arithmetic path above.
+// E4M3): codes with it are detected per word and fixed up, and values
+// derived from them take the exact bit-arithmetic path above.
 // ---------------------------------------------------------------------------
-// True when any byte of the vector has exponent field 15.
-__device__ __forceinline__ bool fp8_any_e15(const u32x4 v) {
-  uint32_t hit = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t t = (v[j] & 0x78787878u) ^ 0x78787878u;  // zero byte <=> e == 15
-    hit |= (t - 0x01010101u) & ~t & 0x80808080u;
-  }
-  return hit != 0;
-}
-
-// 16 codes -> 16 f32 values (exact for exponent fields <= 14).
-__device__ __forceinline__ void decode16_fp8_hw(const u32x4 v, float* x) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w = v[j];
-    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 0x1p-8f, false);
-    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 0x1p-8f, true);
-    x[4 * j] = lo.x;
-    x[4 * j + 1] = lo.y;
-    x[4 * j + 2] = hi.x;
-    x[4 * j + 3] = hi.y;
-  }
-}
-
-// Replaces the values of exponent-15 codes by inf (mantissa 0) or NaN.
-__device__ __forceinline__ void fix_fp8_e15(const u32x4 v, float* x) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t c = (v[j] >> (8 * b)) & 0xFFu;
-      if ((c & 0x78u) == 0x78u) x[4 * j + b] = fp8_to_f32(c);
-    }
-  }
-}
-
 // Finite f32 -> E4M3B15 bits of a pair, packed into the low (HI = false) or
 // high (HI = true) 16 bits of `old`; the other half of `old` is kept.
 template <bool HI>
@@ -232,6 +195,70 @@ __device__ __forceinline__ float round_fp8_hw(float s) {
   const uint32_t c = encode2_fp8_hw<false>(s, s, 0u);
   const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 0x1p-8f, false);
   return d.x;
+}
+
+// ---------------------------------------------------------------------------
+// Word-level access: a lane's share of one rank is D 32-bit words (D = 1, 2
+// or 4), loaded with one non-temporal D-word load.
+// ---------------------------------------------------------------------------
+template <int D> struct WordsT;
+template <> struct WordsT<1> { typedef uint32_t type; };
+template <> struct WordsT<2> { typedef uint32_t type __attribute__((ext_vector_type(2))); };
+template <> struct WordsT<4> { typedef uint32_t type __attribute__((ext_vector_type(4))); };
+
+// Loads unit `unit` (D words) of a buffer.
+template <int D> __device__ __forceinline__ void ld_words(const void* base, uint64_t unit, uint32_t* w) {
+  typedef typename WordsT<D>::type V;
+  const V v = __builtin_nontemporal_load(reinterpret_cast<const V*>(base) + unit);
+  if constexpr (D == 1) {
+    w[0] = v;
+  } else {
+#pragma unroll
+    for (int j = 0; j < D; ++j) w[j] = v[j];
+  }
+}
+
+// Elements of type T in one 32-bit word, widened to f32.
+template <int T> __device__ __forceinline__ void decode_word(uint32_t w, float* x) {
+  if constexpr (T == kF32) {
+    x[0] = __uint_as_float(w);
+  } else if constexpr (T == kF16) {
+    const f32x2 p = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+    x[0] = p.x;
+    x[1] = p.y;
+  } else if constexpr (T == kBF16) {
+    x[0] = __uint_as_float(w << 16);
+    x[1] = __uint_as_float(w & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) x[b] = fp8_to_f32((w >> (8 * b)) & 0xFFu);
+  }
+}
+
+// Four FP8 E4M3B15 codes through the hardware converts (exact for exponent
+// fields <= 14), see the FP8 section above.
+__device__ __forceinline__ void decode_word_fp8_hw(uint32_t w, float* x) {
+  const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 0x1p-8f, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 0x1p-8f, true);
+  x[0] = lo.x;
+  x[1] = lo.y;
+  x[2] = hi.x;
+  x[3] = hi.y;
+}
+
+// True when any byte of the word has exponent field 15.
+__device__ __forceinline__ bool fp8_word_has_e15(uint32_t w) {
+  const uint32_t t = (w & 0x78787878u) ^ 0x78787878u;  // zero byte <=> e == 15
+  return ((t - 0x01010101u) & ~t & 0x80808080u) != 0;
+}
+
+// Replaces the values of exponent-15 codes of one word by inf or NaN.
+__device__ __forceinline__ void fix_fp8_e15_word(uint32_t w, float* x) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t c = (w >> (8 * b)) & 0xFFu;
+    if ((c & 0x78u) == 0x78u) x[b] = fp8_to_f32(c);
+  }
 }
 
 // ---------------------------------------------------------------------------

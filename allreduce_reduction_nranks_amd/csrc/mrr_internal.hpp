@@ -18,9 +18,9 @@ constexpr int kFlagSlots = MRR_PKT_FLAG_SLOTS;
 struct RsagArgs {
   const void* in[kMaxRanks];
   void* out[kMaxRanks];
-  uint64_t chunk_vecs;    // chunk width C in 16-byte input vectors
-  uint64_t total_vecs;    // whole 16-byte input vectors in [0, count)
-  uint64_t tail_begin;    // first element not covered by a whole vector
+  uint64_t chunk_vecs;    // chunk width C in units (16-byte output vectors)
+  uint64_t total_vecs;    // whole units in [0, count)
+  uint64_t tail_begin;    // first element not covered by a whole unit
   uint32_t tail_count;    // elements in the tail handled by this launch (0..15)
   uint32_t first_chunk;   // first chunk of the launch
   uint32_t tiles_per_chunk;

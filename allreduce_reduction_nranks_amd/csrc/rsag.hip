@@ -35,23 +35,23 @@ namespace mrr {
 
 constexpr int kRsagThreads = 64;  // one wave per workgroup
 
-// Launch shape, from a sweep of (vectors per lane U) x (workgroups per CU)
-// of this kernel on MI355X with rank buffers allocated one after another
-// (64 MiB and 256 MiB per rank).  Streaming bandwidth is bumpy in both knobs
-// -- the 2N same-offset streams interact with the DRAM channel and bank
-// mapping -- so each entry is the setting that stayed near the best across
-// buffer sizes rather than a formula.
+// Launch shape, from a sweep of (units per lane U) x (workgroups per CU)
+// of this kernel on MI355X (64 MiB and 256 MiB per rank).  Streaming
+// bandwidth is bumpy in both knobs -- the 2N same-offset streams interact
+// with the DRAM channel and bank mapping -- so each entry is the setting that
+// stayed near the best across buffer sizes rather than a formula.
 //   16-bit and 32-bit inputs: N=2 U=8 x2, N=4 U=4 x4, N=8 U=1 x6,
 //                             N=16 U=2 x2, N=32 U=1 x8 (workgroups per CU)
-//   FP8 inputs (16 elements and accumulators per vector): U=4 for N=2,
-//                             else 1; 4 workgroups per CU for FP8 outputs,
-//                             2 for the wider (write-heavier) outputs.
-constexpr int rsag_unroll(int n, int tin) {
-  if (tin == kFP8) return n == 2 ? 4 : 1;
+//   FP8 inputs: U=4 for N=2, else 1, times 2 for f16 and 4 for f32 outputs
+//                             (so a lane still loads 16 bytes per rank);
+//                             workgroups per CU: 4 (FP8 out), 3 (f16 out),
+//                             4 (f32 out).
+constexpr int rsag_unroll(int n, int tin, int tout) {
+  if (tin == kFP8) return (n == 2 ? 4 : 1) * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
   return n == 2 ? 8 : n == 4 ? 4 : n == 16 ? 2 : 1;
 }
 constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
-  if (tin == kFP8) return tout == kFP8 ? 4 : 2;
+  if (tin == kFP8) return tout == kF16 ? 3 : 4;
   return n == 2 ? 2 : n == 4 ? 4 : n == 8 ? 6 : n == 16 ? 2 : 8;
 }
 // Ranks whose vectors are loaded together before they are added: all of them
@@ -70,51 +70,64 @@ __device__ __forceinline__ void reduce_elem(const void* const* in, void* const* 
   for (int k = 0; k < n; ++k) store_elem<Out>(out[k], i, acc);
 }
 
-// Reduces UU vector positions v0 + u * kRsagThreads (u < UU) over the N ranks
-// and stores each result to all N outputs.  The first partial sum is x_0
-// rounded to the accumulator type (the identity except for an FP8
-// accumulator, which saturates an infinite x_0 like any later sum).  Ranks
-// are taken in groups of G: the group's UU * G loads are all issued before
-// the first add of the group, then the adds run in rank order.
+// A unit is one 16-byte output vector: UE = 16 / size(Out) elements, whose
+// inputs are D = UE * size(In) / 4 words per rank (4, 2 or 1).  Keeping the
+// output side at 16 bytes per lane makes every store instruction write 1 KiB
+// of contiguous memory, whatever the input width.
+template <int In, int Out> struct Unit {
+  static constexpr int UE = 16 / Ty<Out>::size;
+  static constexpr int D = UE * Ty<In>::size / 4;
+  static constexpr int EPW = 4 / Ty<In>::size;  // elements per input word
+};
+
+// Reduces UU units v0 + u * kRsagThreads (u < UU) over the N ranks and stores
+// each result to all N outputs.  The first partial sum is x_0 rounded to the
+// accumulator type (the identity except for an FP8 accumulator, which
+// saturates an infinite x_0 like any later sum).  Ranks are taken in groups
+// of G: the group's UU * G loads are all issued before the first add of the
+// group, then the adds run in rank order.
 //
-// FP8 inputs decode through the hardware E4M3 converts; a lane whose vectors
-// hold an exponent-15 code (inf / NaN) marks that position `special`, fixes
-// those values, and rounds / encodes that position with the exact bit
-// arithmetic instead of the converts, which are only exact for finite data.
+// FP8 inputs decode through the hardware E4M3 converts; a lane whose words
+// hold an exponent-15 code (inf / NaN) marks that unit `special`, fixes
+// those values, and rounds / encodes that unit with the exact bit arithmetic
+// instead of the converts, which are only exact for finite data.
 template <int N, int In, int Acc, int Out, int UU, int G>
 __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
-  constexpr int VW = Vec<In>::VW;
-  constexpr int OV = Ty<Out>::size / Ty<In>::size;  // output vectors per input vector
-  constexpr int OW = Vec<Out>::VW;                  // elements per output vector
+  constexpr int UE = Unit<In, Out>::UE;
+  constexpr int D = Unit<In, Out>::D;
+  constexpr int EPW = Unit<In, Out>::EPW;
   static_assert(N % G == 0, "rank group must divide N");
-  float acc[UU][VW];
+  float acc[UU][UE];
   bool special[UU];
 #pragma unroll
   for (int u = 0; u < UU; ++u) special[u] = false;
 #pragma unroll(N / G <= 2 ? N / G : 1)
   for (int g = 0; g < N; g += G) {
-    u32x4 raw[UU][G];
+    uint32_t raw[UU][G][D];
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
 #pragma unroll
-      for (int r = 0; r < G; ++r) raw[u][r] = ld_stream(a.in[g + r], v0 + (uint64_t)u * kRsagThreads);
+      for (int r = 0; r < G; ++r) ld_words<D>(a.in[g + r], v0 + (uint64_t)u * kRsagThreads, raw[u][r]);
     }
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
 #pragma unroll
       for (int r = 0; r < G; ++r) {
-        float x[VW];
-        if constexpr (In == kFP8) {
-          decode16_fp8_hw(raw[u][r], x);
-          if (fp8_any_e15(raw[u][r])) {
-            fix_fp8_e15(raw[u][r], x);
-            special[u] = true;
+        float x[UE];
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          if constexpr (In == kFP8) {
+            decode_word_fp8_hw(raw[u][r][j], x + j * EPW);
+            if (fp8_word_has_e15(raw[u][r][j])) {
+              fix_fp8_e15_word(raw[u][r][j], x + j * EPW);
+              special[u] = true;
+            }
+          } else {
+            decode_word<In>(raw[u][r][j], x + j * EPW);
           }
-        } else {
-          decode16<In>(raw[u][r], x);
         }
 #pragma unroll
-        for (int j = 0; j < VW; ++j) {
+        for (int j = 0; j < UE; ++j) {
           const float s = g + r == 0 ? x[j] : acc[u][j] + x[j];
           if constexpr (Acc == kFP8) acc[u][j] = special[u] ? round_acc<kFP8>(s) : round_fp8_hw(s);
           else acc[u][j] = round_acc<Acc>(s);
@@ -125,17 +138,11 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
 #pragma unroll
   for (int u = 0; u < UU; ++u) {
     const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
-    u32x4 o[OV];
+    u32x4 o;
+    if constexpr (Out == kFP8) o = special[u] ? encode16<kFP8>(acc[u]) : encode16_fp8_hw(acc[u]);
+    else o = encode16<Out>(acc[u]);
 #pragma unroll
-    for (int q = 0; q < OV; ++q) {
-      if constexpr (Out == kFP8) o[q] = special[u] ? encode16<kFP8>(acc[u] + q * OW) : encode16_fp8_hw(acc[u] + q * OW);
-      else o[q] = encode16<Out>(acc[u] + q * OW);
-    }
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-#pragma unroll
-      for (int q = 0; q < OV; ++q) st_stream(a.out[k], v * OV + q, o[q]);
-    }
+    for (int k = 0; k < N; ++k) st_stream(a.out[k], v, o);
   }
 }
 
@@ -199,7 +206,7 @@ static void launch_vec_typed(int nranks, dim3 grid, const RsagArgs& a, hipStream
   switch (nranks) {
 #define MRR_CASE(N)                                                                        \
   case N:                                                                                  \
-    hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In)>), grid, block, \
+    hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In, Out)>), grid, block, \
                        0, s, a);                                                           \
     break;
     MRR_CASE(2) MRR_CASE(4) MRR_CASE(8) MRR_CASE(16) MRR_CASE(32)
@@ -216,7 +223,8 @@ static void launch_scalar_typed(dim3 grid, const RsagScalarArgs& a, hipStream_t 
 hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const* outputs,
                        hipStream_t stream) {
   const int n = p.nranks;
-  const uint64_t vw = 16 / type_size(p.tin);
+  const uint64_t vw = 16 / type_size(p.tin);   // chunk granularity: 16-byte input vectors
+  const uint64_t ue = 16 / type_size(p.tout);  // elements per unit (16-byte output vector)
   const uint64_t count = p.count;
   // Chunk width: ceil(count / N) rounded up to whole 16-byte input vectors.
   const uint64_t per = (count + n - 1) / n;
@@ -228,12 +236,12 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
       a.in[r] = inputs[r];
       a.out[r] = outputs[r];
     }
-    a.chunk_vecs = chunk_elems / vw;
-    a.total_vecs = count / vw;
-    a.tail_begin = a.total_vecs * vw;
+    a.chunk_vecs = chunk_elems / ue;  // whole units: ue divides vw
+    a.total_vecs = count / ue;
+    a.tail_begin = a.total_vecs * ue;
     const uint32_t tail = (uint32_t)(count - a.tail_begin);
     const uint64_t tail_chunk = a.total_vecs / a.chunk_vecs;
-    const uint64_t tile_vecs = (uint64_t)kRsagThreads * rsag_unroll(n, p.tin);
+    const uint64_t tile_vecs = (uint64_t)kRsagThreads * rsag_unroll(n, p.tin, p.tout);
     a.tiles_per_chunk = (uint32_t)((a.chunk_vecs + tile_vecs - 1) / tile_vecs);
     uint32_t nchunks;
     if (p.rank < 0) {

@@ -145,8 +145,20 @@ def bench_rsag(args, torch, mrr, synth):
     count = per_rank // ESIZE[t]
     gen_dev = "cuda" if n * count > (1 << 26) else "cpu"
     log("config", args.config, "n", n, "type", t, "->", tout, "count", count, "inputs drawn on", gen_dev)
-    ins = [x.to("cuda") for x in synth.rank_inputs(kind, t, n, count, args.seed0, device=gen_dev)]
-    outs = [torch.empty(count * ESIZE[tout], dtype=torch.uint8, device="cuda") for _ in range(n)]
+    ins_sep = [x.to("cuda") for x in synth.rank_inputs(kind, t, n, count, args.seed0, device=gen_dev)]
+    outs_sep = [torch.empty(count * ESIZE[tout], dtype=torch.uint8, device="cuda") for _ in range(n)]
+    if args.layout == "pitch":
+        # The library's recommended HBM placement: each side's N rank buffers
+        # in one allocation, mrr_rank_buffer_pitch() bytes apart.
+        _, ins = mrr.alloc_rank_buffers(n, count, t)
+        for dst, src in zip(ins, ins_sep):
+            dst.view(torch.uint8).copy_(src.view(torch.uint8))
+        _, outs = mrr.alloc_rank_buffers(n, count, tout)
+        layout = ("one allocation per side, rank buffers %d B apart (mrr_rank_buffer_pitch)"
+                  % mrr.mrr_rank_buffer_pitch(count * ESIZE[t], n))
+    else:
+        ins, outs = ins_sep, outs_sep
+        layout = "one allocation per rank buffer"
     torch.cuda.synchronize()
 
     def step():
@@ -155,6 +167,13 @@ def bench_rsag(args, torch, mrr, synth):
             raise mrr.MrrError(st)
 
     wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    sep_us = None
+    if args.layout == "pitch":
+        def step_sep():
+            st = mrr.mrr_allreduce_rsag_ex(ins_sep, outs_sep, count, t, acc, tout, n, -1)
+            if st != mrr.MRR_OK:
+                raise mrr.MrrError(st)
+        sep_us = Timer(torch).run(step_sep, args.steps, args.warmup)[1] * 1e3
     alg_bytes = n * count * (ESIZE[t] + ESIZE[tout])
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
@@ -178,13 +197,15 @@ def bench_rsag(args, torch, mrr, synth):
         "config": {"workload": workload, "nranks": n, "bytes_per_rank": count * ESIZE[t],
                    "count": count, "in": t, "accum": acc, "out": tout,
                    "algorithmic_bytes_per_call": alg_bytes, "kernel_us": round(kern_ms * 1e3, 2),
-                   "pct_of_hbm_peak": round(100 * value / PEAK_GBPS, 2)},
+                   "pct_of_hbm_peak": round(100 * value / PEAK_GBPS, 2), "layout": layout},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": traffic},
     }
     if ceiling is not None:
         result["config"]["copy_ceiling_gbps"] = round(ceiling, 2)
+    if sep_us is not None:
+        result["config"]["kernel_us_one_allocation_per_rank"] = round(sep_us, 2)
     if args.cpu_baseline:
         sample = min(count, args.cpu_sample)
         result["cpu_baseline"] = cpu_baseline_rsag(ins, t, acc, tout, sample)
@@ -236,6 +257,9 @@ def main():
     ap.add_argument("--blocks", type=int, default=0, help="c3: blocks per rank (0 = auto)")
     ap.add_argument("--threads", type=int, default=0, help="c3: threads (0 = auto)")
     ap.add_argument("--seed0", type=int, default=0)
+    ap.add_argument("--layout", default="pitch", choices=["pitch", "separate"],
+                    help="rank buffer placement: one allocation per side at mrr_rank_buffer_pitch() "
+                         "spacing (default), or one allocation per buffer")
     ap.add_argument("--cpu-sample", type=int, default=1 << 30,
                     help="elements per rank the CPU oracle baseline reduces")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")

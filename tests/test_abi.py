@@ -188,3 +188,16 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.lower(), f
+
+
+def test_rank_buffer_pitch(lib):
+    MiB = 1 << 20
+    assert mrr.mrr_rank_buffer_pitch(0, 8) == 0 and mrr.mrr_rank_buffer_pitch(100, 0) == 0
+    assert mrr.mrr_rank_buffer_pitch(1, 8) == 8192
+    assert mrr.mrr_rank_buffer_pitch(64 * MiB, 8) == 64 * MiB + 4096
+    assert mrr.mrr_rank_buffer_pitch(64 * MiB, 16) == 64 * MiB + 2048
+    assert mrr.mrr_rank_buffer_pitch(64 * MiB + 1, 2) == 64 * MiB + 8192
+    for n in (2, 4, 8, 16, 32):
+        for b in (4095, 4096, 4097, 12345, 256 * MiB):
+            p = mrr.mrr_rank_buffer_pitch(b, n)
+            assert p % 16 == 0 and p >= b + 2048 and p < b + 8192

@@ -139,6 +139,20 @@ def test_special_values():
                       "special fp8 %s/%s" % (acc, tout))
 
 
+@pytest.mark.parametrize("t,tout", [("f16", "f16"), ("fp8", "fp8"), ("fp8", "f16")])
+def test_pooled_rank_buffers(t, tout):
+    """Rank buffers carved from one allocation at mrr_rank_buffer_pitch()."""
+    n, count = 8, 3 * 65536 + 7
+    announce("rsag pooled", t, tout)
+    src = inputs_for(t, n, count, seed0=44)
+    _, ins = mrr.alloc_rank_buffers(n, count, t)
+    for d, x in zip(ins, src):
+        d.copy_(x)
+    _, outs = mrr.alloc_rank_buffers(n, count, tout)
+    run(ins, t, "f32", tout, outs=outs)
+    check_all(outs, oracle.allreduce([bits(x) for x in src], t, "f32", tout), tout, "pooled")
+
+
 def test_rank_order_pin():
     """x_0 = 1, x_1..7 = 2^-24 in f32: only the sequential rank order gives 1.0."""
     announce("rsag order pin")
