@@ -62,6 +62,7 @@ def load_library() -> ctypes.CDLL:
             "mrr_allreduce_packet": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, vp], i),
             "mrr_allreduce_packet_ex": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, i, i, vp], i),
             "mrr_packet_reduce": ([pp, vp, sz, i, i, i, u32, u32, u32, vp, vp], i),
+            "mrr_allreduce": ([pp, pp, sz, i, i, i, vp, sz, vp, sz, u32, vp, vp], i),
             "mrr_pack": ([vp, vp, sz, u32, vp], i),
             "mrr_unpack": ([vp, vp, sz, vp], i),
             "mrr_fp8b15_to_f16": ([vp, vp, sz, vp], i),
@@ -179,6 +180,14 @@ def mrr_allreduce_packet_ex(inputs, outputs, scratch, scratch_bytes, flags, coun
         _ptrs(inputs), _ptrs(outputs), _ptr(scratch), scratch_bytes, _ptr(flags), count,
         _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), blocks_per_rank, threads,
         _stream(stream))
+
+
+def mrr_allreduce(inputs, outputs, count, dtype, accum, nranks, scratch=None, scratch_bytes=0,
+                  flags=None, packet_max_bytes=0, max_spins=0, dev_err=None, stream=None) -> int:
+    return load_library().mrr_allreduce(_ptrs(inputs), _ptrs(outputs), count, _dt(dtype),
+                                        _dt(accum), nranks, _ptr(scratch), scratch_bytes,
+                                        _ptr(flags), packet_max_bytes, max_spins, _ptr(dev_err),
+                                        _stream(stream))
 
 
 def mrr_packet_reduce(in_pkts, out_pkts, npkts, dtype, accum, nranks, flag_in, flag_out,

@@ -123,17 +123,19 @@ size_t mrr_rank_buffer_pitch(size_t bytes_per_rank, int nranks) {
   return (bytes_per_rank + page - 1) / page * page + stagger;
 }
 
-mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs, size_t count,
-                                 mrr_dtype in, mrr_dtype accum, mrr_dtype out, int nranks,
-                                 int rank, void* stream) {
-  static const char* fn = "mrr_allreduce_rsag";
-  if (!valid_nranks(nranks)) return refuse(MRR_EUNSUPPORTED, fn, "nranks not in {2,4,8,16,32}");
+// Shared by mrr_allreduce_rsag_ex (compiled rank counts only, as the RS/AG
+// algorithm is specified) and mrr_allreduce (any count in [1, 32]).
+static mrr_status rsag_call(const char* fn, const void* const* inputs, void* const* outputs,
+                            size_t count, mrr_dtype in, mrr_dtype accum, mrr_dtype out, int nranks,
+                            int rank, void* stream, bool any_n) {
+  if (any_n ? (nranks < 1 || nranks > MRR_MAX_RANKS) : !valid_nranks(nranks))
+    return refuse(MRR_EUNSUPPORTED, fn, any_n ? "nranks outside [1, 32]" : "nranks not in {2,4,8,16,32}");
   if (rank < -1 || rank >= nranks) return refuse(MRR_EINVAL, fn, "rank outside [-1, nranks)");
   if (!inputs || !outputs) return refuse(MRR_EINVAL, fn, "null pointer array");
   const int tin = (int)in;
   const int tacc = accum == MRR_AUTO ? tin : (int)accum;
   const int tout = out == MRR_AUTO ? tin : (int)out;
-  if (!tsize(tin) || !rsag_supported(nranks, tin, tacc, tout))
+  if (!tsize(tin) || !rsag_types_supported(tin, tacc, tout))
     return refuse(MRR_EUNSUPPORTED, fn, "type combination");
   if (count == 0) return MRR_OK;
   const size_t ein = tsize(tin), eout = tsize(tout);
@@ -150,6 +152,13 @@ mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs
     return refuse(MRR_EOVERLAP, fn, "output overlaps another buffer");
   RsagPlan plan{nranks, tin, tacc, tout, count, rank, vec};
   return hip_status(launch_rsag(plan, inputs, outputs, (hipStream_t)stream), fn);
+}
+
+mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs, size_t count,
+                                 mrr_dtype in, mrr_dtype accum, mrr_dtype out, int nranks,
+                                 int rank, void* stream) {
+  return rsag_call("mrr_allreduce_rsag", inputs, outputs, count, in, accum, out, nranks, rank,
+                   stream, false);
 }
 
 mrr_status mrr_allreduce_rsag(const void* const* inputs, void* const* outputs, size_t count,
@@ -252,6 +261,24 @@ mrr_status mrr_allreduce_packet(const void* const* inputs, void* const* outputs,
                                 uint32_t max_spins, uint32_t* dev_err, void* stream) {
   return mrr_allreduce_packet_ex(inputs, outputs, scratch, scratch_bytes, flags, count, dtype,
                                  accum, nranks, max_spins, dev_err, 0, 0, stream);
+}
+
+mrr_status mrr_allreduce(const void* const* inputs, void* const* outputs, size_t count,
+                         mrr_dtype dtype, mrr_dtype accum, int nranks, void* scratch,
+                         size_t scratch_bytes, uint32_t* flags, size_t packet_max_bytes,
+                         uint32_t max_spins, uint32_t* dev_err, void* stream) {
+  static const char* fn = "mrr_allreduce";
+  if (nranks < 1 || nranks > MRR_MAX_RANKS) return refuse(MRR_EUNSUPPORTED, fn, "nranks outside [1, 32]");
+  const int t = (int)dtype;
+  const int tacc = accum == MRR_AUTO ? t : (int)accum;
+  const size_t e = tsize(t);
+  const bool packets = valid_nranks(nranks) && scratch && flags && e && count > 0 &&
+                       count <= packet_max_bytes / e && packet_supported(nranks, t, tacc) &&
+                       scratch_bytes >= mrr_packet_scratch_bytes(count, dtype, nranks);
+  if (packets)
+    return mrr_allreduce_packet(inputs, outputs, scratch, scratch_bytes, flags, count, dtype,
+                                accum, nranks, max_spins, dev_err, stream);
+  return rsag_call(fn, inputs, outputs, count, dtype, accum, MRR_AUTO, nranks, -1, stream, true);
 }
 
 mrr_status mrr_packet_reduce(const uint64_t* const* in_pkts, uint64_t* out_pkts, size_t npkts,

@@ -25,6 +25,8 @@ struct RsagArgs {
   uint32_t first_chunk;   // first chunk of the launch
   uint32_t tiles_per_chunk;
   uint32_t launch_tiles;  // tiles of all chunks in the launch
+  uint32_t nranks;        // rank count (read by the runtime-N kernel)
+  uint32_t pad;
 };
 
 // Element-wise kernel arguments (pointers not 16-byte aligned).
@@ -42,6 +44,12 @@ struct RsagPlan {
   int rank;             // -1 = all chunks
   bool vector;          // every pointer 16-byte aligned
 };
+
+// True for the rank counts with a compile-time kernel (2, 4, 8, 16, 32); any
+// other count in [1, kMaxRanks] runs the runtime-N kernel.
+bool rsag_compiled_nranks(int n);
+// Type combination check independent of the rank count.
+bool rsag_types_supported(int tin, int tacc, int tout);
 
 hipError_t launch_rsag(const RsagPlan& plan, const void* const* inputs, void* const* outputs,
                        hipStream_t stream);

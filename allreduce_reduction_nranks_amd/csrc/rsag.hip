@@ -171,6 +171,88 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a
     reduce_elem<In, Acc, Out>(a.in, a.out, N, a.tail_begin + threadIdx.x);
 }
 
+// Runtime rank count (1..32): the fallback for counts without a compiled
+// kernel.  Ranks are taken in groups of 8 behind wavefront-uniform bounds,
+// in rank order, with the same unit structure as reduce_store.
+constexpr int kAnyGroup = 8;
+
+template <int In, int Acc, int Out, int UU>
+__device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint64_t v0) {
+  constexpr int UE = Unit<In, Out>::UE;
+  constexpr int D = Unit<In, Out>::D;
+  constexpr int EPW = Unit<In, Out>::EPW;
+  float acc[UU][UE];
+  bool special[UU];
+#pragma unroll
+  for (int u = 0; u < UU; ++u) special[u] = false;
+  for (int g = 0; g < n; g += kAnyGroup) {
+    uint32_t raw[UU][kAnyGroup][D];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+#pragma unroll
+      for (int r = 0; r < kAnyGroup; ++r)
+        if (g + r < n) ld_words<D>(a.in[g + r], v0 + (uint64_t)u * kRsagThreads, raw[u][r]);
+    }
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+#pragma unroll
+      for (int r = 0; r < kAnyGroup; ++r) {
+        if (g + r >= n) break;
+        float x[UE];
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          if constexpr (In == kFP8) {
+            decode_word_fp8_hw(raw[u][r][j], x + j * EPW);
+            if (fp8_word_has_e15(raw[u][r][j])) {
+              fix_fp8_e15_word(raw[u][r][j], x + j * EPW);
+              special[u] = true;
+            }
+          } else {
+            decode_word<In>(raw[u][r][j], x + j * EPW);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < UE; ++j) {
+          const float s = g + r == 0 ? x[j] : acc[u][j] + x[j];
+          if constexpr (Acc == kFP8) acc[u][j] = special[u] ? round_acc<kFP8>(s) : round_fp8_hw(s);
+          else acc[u][j] = round_acc<Acc>(s);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UU; ++u) {
+    const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
+    u32x4 o;
+    if constexpr (Out == kFP8) o = special[u] ? encode16<kFP8>(acc[u]) : encode16_fp8_hw(acc[u]);
+    else o = encode16<Out>(acc[u]);
+    for (int k = 0; k < n; ++k) st_stream(a.out[k], v, o);
+  }
+}
+
+template <int In, int Acc, int Out, int U>
+__global__ void __launch_bounds__(kRsagThreads) rsag_any_kernel(const RsagArgs a) {
+  const int n = (int)a.nranks;
+  for (uint32_t i = blockIdx.x; i < a.launch_tiles; i += gridDim.x) {
+    const uint32_t chunk_rel = i / a.tiles_per_chunk;
+    const uint32_t tile = i - chunk_rel * a.tiles_per_chunk;
+    const uint64_t v_lo = (uint64_t)(a.first_chunk + chunk_rel) * a.chunk_vecs;
+    const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
+    const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
+    if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
+      reduce_store_any<In, Acc, Out, U>(a, n, v0);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
+        if (v < v_hi) reduce_store_any<In, Acc, Out, 1>(a, n, v);
+      }
+    }
+  }
+  if (a.tail_count != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < a.tail_count)
+    reduce_elem<In, Acc, Out>(a.in, a.out, n, a.tail_begin + threadIdx.x);
+}
+
 // Element-wise variant for buffers that are not 16-byte aligned.
 template <int In, int Acc, int Out>
 __global__ void __launch_bounds__(256) rsag_scalar_kernel(const RsagScalarArgs a) {
@@ -190,12 +272,17 @@ __global__ void __launch_bounds__(256) rsag_scalar_kernel(const RsagScalarArgs a
 
 static bool valid_nranks(int n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32; }
 
-bool rsag_supported(int nranks, int tin, int tacc, int tout) {
-  if (!valid_nranks(nranks)) return false;
+bool rsag_compiled_nranks(int n) { return valid_nranks(n); }
+
+bool rsag_types_supported(int tin, int tacc, int tout) {
 #define MRR_MATCH(I, A, O) if (tin == I && tacc == A && tout == O) return true;
   MRR_RSAG_TRIPLES(MRR_MATCH)
 #undef MRR_MATCH
   return false;
+}
+
+bool rsag_supported(int nranks, int tin, int tacc, int tout) {
+  return valid_nranks(nranks) && rsag_types_supported(tin, tacc, tout);
 }
 
 static int type_size(int t) { return t == kF32 ? 4 : (t == kFP8 ? 1 : 2); }
@@ -213,6 +300,19 @@ static void launch_vec_typed(int nranks, dim3 grid, const RsagArgs& a, hipStream
 #undef MRR_CASE
     default: break;
   }
+}
+
+// The runtime-N kernel loads 16 bytes per lane per rank like the compiled
+// ones at N = 8; one unit per lane, 6 workgroups per CU.
+constexpr int rsag_any_unroll(int tin, int tout) {
+  return tin == kFP8 ? (tout == kF32 ? 4 : tout == kF16 ? 2 : 1) : 1;
+}
+constexpr int kAnyWgPerCu = 6;
+
+template <int In, int Acc, int Out>
+static void launch_any_typed(dim3 grid, const RsagArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, rsag_any_unroll(In, Out)>), grid,
+                     dim3(kRsagThreads), 0, s, a);
 }
 
 template <int In, int Acc, int Out>
@@ -241,7 +341,10 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
     a.tail_begin = a.total_vecs * ue;
     const uint32_t tail = (uint32_t)(count - a.tail_begin);
     const uint64_t tail_chunk = a.total_vecs / a.chunk_vecs;
-    const uint64_t tile_vecs = (uint64_t)kRsagThreads * rsag_unroll(n, p.tin, p.tout);
+    const bool any_n = !valid_nranks(n);
+    a.nranks = (uint32_t)n;
+    const uint64_t tile_vecs =
+        (uint64_t)kRsagThreads * (any_n ? rsag_any_unroll(p.tin, p.tout) : rsag_unroll(n, p.tin, p.tout));
     a.tiles_per_chunk = (uint32_t)((a.chunk_vecs + tile_vecs - 1) / tile_vecs);
     uint32_t nchunks;
     if (p.rank < 0) {
@@ -255,7 +358,7 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
     }
     a.launch_tiles = nchunks * a.tiles_per_chunk;
     // Persistent grid: wg_per_cu workgroups per CU (MRR_RSAG_WPC overrides).
-    int wpc = rsag_wg_per_cu(n, p.tin, p.tout);
+    int wpc = any_n ? kAnyWgPerCu : rsag_wg_per_cu(n, p.tin, p.tout);
     static const int wpc_env = [] {
       const char* v = getenv("MRR_RSAG_WPC");
       return v ? atoi(v) : 0;
@@ -265,10 +368,17 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
     if (blocks == 0) blocks = 1024;
     if (blocks > a.launch_tiles) blocks = a.launch_tiles;
     const dim3 grid((uint32_t)blocks);
+    if (any_n) {
+#define MRR_DISPATCH(I, A, O) \
+  if (p.tin == I && p.tacc == A && p.tout == O) launch_any_typed<I, A, O>(grid, a, stream);
+      MRR_RSAG_TRIPLES(MRR_DISPATCH)
+#undef MRR_DISPATCH
+    } else {
 #define MRR_DISPATCH(I, A, O) \
   if (p.tin == I && p.tacc == A && p.tout == O) launch_vec_typed<I, A, O>(n, grid, a, stream);
-    MRR_RSAG_TRIPLES(MRR_DISPATCH)
+      MRR_RSAG_TRIPLES(MRR_DISPATCH)
 #undef MRR_DISPATCH
+    }
   } else {
     RsagScalarArgs a = {};
     for (int r = 0; r < n; ++r) {

@@ -15,7 +15,8 @@ CPU oracle on a bounded sample of the same workload.
 
 Other configurations (--config): c1 (2 x 1 MiB bf16), c3 (LL-packet allpair,
 8 ranks, --size KiB), c4 (8 x 32 MiB FP8 E4M3B15 -> f16 or fp8 via --out),
-c5 (N x 256 MiB bf16 via --nranks).
+c5 (N x 256 MiB bf16 via --nranks), custom (--nranks N --size KiB --dtype T; rank
+counts outside 2/4/8/16/32 run the runtime-N kernel through mrr_allreduce).
 """
 from __future__ import annotations
 
@@ -138,6 +139,10 @@ def bench_rsag(args, torch, mrr, synth):
         n, t, per_rank = args.nranks, "bf16", 256 * MiB
         tout, acc = t, "f32"
         kind = "normal"
+    elif args.config == "custom":
+        n, t, per_rank = args.nranks, args.dtype, args.size * 1024
+        tout, acc = (args.out if args.dtype == "fp8" else t), "f32"
+        kind = "fp8codes" if t == "fp8" else "normal"
     else:
         n, t, per_rank = 8, "f16", 64 * MiB
         tout, acc = t, "f32"
@@ -161,8 +166,13 @@ def bench_rsag(args, torch, mrr, synth):
         layout = "one allocation per rank buffer"
     torch.cuda.synchronize()
 
+    compiled = n in (2, 4, 8, 16, 32)
+
     def step():
-        st = mrr.mrr_allreduce_rsag_ex(ins, outs, count, t, acc, tout, n, -1)
+        if compiled:
+            st = mrr.mrr_allreduce_rsag_ex(ins, outs, count, t, acc, tout, n, -1)
+        else:  # rank counts without a compiled kernel: the runtime-N RS/AG
+            st = mrr.mrr_allreduce(ins, outs, count, t, acc, n)
         if st != mrr.MRR_OK:
             raise mrr.MrrError(st)
 
@@ -170,7 +180,8 @@ def bench_rsag(args, torch, mrr, synth):
     sep_us = None
     if args.layout == "pitch":
         def step_sep():
-            st = mrr.mrr_allreduce_rsag_ex(ins_sep, outs_sep, count, t, acc, tout, n, -1)
+            st = mrr.mrr_allreduce_rsag_ex(ins_sep, outs_sep, count, t, acc, tout, n, -1) \
+                if compiled else mrr.mrr_allreduce(ins_sep, outs_sep, count, t, acc, n)
             if st != mrr.MRR_OK:
                 raise mrr.MrrError(st)
         sep_us = Timer(torch).run(step_sep, args.steps, args.warmup)[1] * 1e3
@@ -178,7 +189,8 @@ def bench_rsag(args, torch, mrr, synth):
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     key = {"c1": "rsag_2x1MiB_bf16", "c2": "rsag_8x64MiB_f16",
-           "c4": "rsag_8x32MiB_fp8_to_%s" % tout, "c5": "rsag_%dx256MiB_bf16" % n}[args.config]
+           "c4": "rsag_8x32MiB_fp8_to_%s" % tout, "c5": "rsag_%dx256MiB_bf16" % n,
+           "custom": "rsag_%dx%dKiB_%s" % (n, args.size, t)}[args.config]
     traffic = measured_traffic(key)
     ceiling = copy_ceiling(torch, n * count * ESIZE[t]) if args.copy_ceiling else None
     workload = {"c1": "RS/AG allreduce, 2 ranks x 1 MiB bf16 ~N(0,1), fp32 accumulation",
@@ -186,8 +198,9 @@ def bench_rsag(args, torch, mrr, synth):
                       "reduced chunks written to all 8 outputs",
                 "c4": "RS/AG allreduce, 8 ranks x 32 MiB FP8 E4M3B15 finite codes, fp32 "
                       "accumulation, %s outputs" % tout,
-                "c5": "RS/AG allreduce, %d ranks x 256 MiB bf16 ~N(0,1), fp32 accumulation" % n}[
-        args.config]
+                "c5": "RS/AG allreduce, %d ranks x 256 MiB bf16 ~N(0,1), fp32 accumulation" % n,
+                "custom": "RS/AG allreduce, %d ranks x %d KiB %s, fp32 accumulation, %s outputs"
+                          % (n, args.size, t, tout)}[args.config]
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
@@ -250,10 +263,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "custom"])
+    ap.add_argument("--dtype", default="f16", choices=["f32", "f16", "bf16", "fp8"], help="custom: type")
     ap.add_argument("--nranks", type=int, default=8, help="c5: rank count")
     ap.add_argument("--out", default="f16", choices=["f16", "fp8", "f32"], help="c4: output type")
-    ap.add_argument("--size", type=int, default=1024, help="c3: KiB per rank")
+    ap.add_argument("--size", type=int, default=1024, help="c3 / custom: KiB per rank")
     ap.add_argument("--blocks", type=int, default=0, help="c3: blocks per rank (0 = auto)")
     ap.add_argument("--threads", type=int, default=0, help="c3: threads (0 = auto)")
     ap.add_argument("--seed0", type=int, default=0)

@@ -76,6 +76,14 @@ typedef enum mrr_dtype {
   MRR_FP8_E4M3B15 = 4
 } mrr_dtype;
 
+/* Packet / RS-AG crossover for mrr_allreduce, measured on one MI355X: 0.
+ * There RS/AG is faster at every size (8 ranks of f16: 10.7 us against
+ * 12.2-12.7 us up to 64 KiB per rank, 11.2 us against 51.5 us at 1 MiB),
+ * because within one GPU it needs no cross-rank synchronisation while
+ * packets double the bytes moved.  The pages' selectors, spanning GPUs,
+ * switch to RS/AG above 512 KiB (Python default) or 2 MiB (NCCL shim). */
+#define MRR_PACKET_MAX_BYTES_ONE_GPU 0
+
 /* Largest rank count any entry point accepts. */
 #define MRR_MAX_RANKS 32
 /* Flag slots per rank in a packet flag buffer. */
@@ -178,6 +186,29 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
                                    mrr_dtype dtype, mrr_dtype accum, int nranks,
                                    uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
                                    int threads, void* stream);
+
+/* --------------------------------------------------------------------------
+ * One-call allreduce with algorithm selection ("Support 2 ranks in
+ * AllreduceRsAgZeroCopy", section "why": selectors pick RS/AG zero-copy above
+ * a message size and packets below it; section "what changed": rank counts
+ * the RS/AG kernel does not cover could fall back to another algorithm).
+ *
+ * out type == dtype; accum as for the packet path (AUTO = dtype).
+ *   - nranks in {2,4,8,16,32}, scratch and flags non-NULL, scratch_bytes >=
+ *     mrr_packet_scratch_bytes(), count * elem_size <= packet_max_bytes and
+ *     the (dtype, accum) pair has a packet kernel: the LL-packet allpair
+ *     (same contract as mrr_allreduce_packet).
+ *   - otherwise RS/AG over all chunks; a rank count in [1, 32] without a
+ *     compiled kernel (1, 3, 5, 6, 7, 9, ...) runs the runtime-N RS/AG kernel,
+ *     with the same results (sum in rank order 0..N-1).
+ * MRR_PACKET_MAX_BYTES_ONE_GPU is the crossover measured on one MI355X (see
+ * its definition); callers sharing work over several GPUs pick their own.
+ * Errors as for the chosen path; nranks outside [1, 32] -> MRR_EUNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+mrr_status mrr_allreduce(const void* const* inputs, void* const* outputs, size_t count,
+                         mrr_dtype dtype, mrr_dtype accum, int nranks, void* scratch,
+                         size_t scratch_bytes, uint32_t* flags, size_t packet_max_bytes,
+                         uint32_t max_spins, uint32_t* dev_err, void* stream);
 
 /* Receive step alone: for every k < npkts, wait until in_pkts[s][k] carries
  * flag_in for every s, sum the payload elements (4 / elem_size per word) in

@@ -201,3 +201,21 @@ def test_rank_buffer_pitch(lib):
         for b in (4095, 4096, 4097, 12345, 256 * MiB):
             p = mrr.mrr_rank_buffer_pitch(b, n)
             assert p % 16 == 0 and p >= b + 2048 and p < b + 8192
+
+
+def test_allreduce_dispatch_checks(lib):
+    ins = [fake(r) for r in range(33)]
+    outs = [fake(64 + r) for r in range(33)]
+    for n in (0, 33, -1):
+        assert mrr.mrr_allreduce(ins[:max(n, 1)], outs[:max(n, 1)], 1024, "f16", "f32", n,
+                                 stream=0) == mrr.MRR_EUNSUPPORTED
+    # rank counts outside {2,4,8,16,32} are accepted (runtime-N RS/AG); check the
+    # validation reaches the buffers: an odd address is refused before any launch
+    for n in (1, 3, 5, 7, 12, 31):
+        bad = list(ins[:n])
+        bad[0] += 1
+        assert mrr.mrr_allreduce(bad, outs[:n], 1024, "f16", "f32", n, stream=0) == mrr.MRR_EALIGN
+        assert mrr.mrr_allreduce(ins[:n], outs[:n], 0, "f16", "f32", n, stream=0) == mrr.MRR_OK
+    # the RS/AG entry itself keeps the pages' rank-count contract
+    assert rsag(3, ins=ins[:3], outs=outs[:3]) == mrr.MRR_EUNSUPPORTED
+    assert mrr.mrr_allreduce(ins[:4], outs[:4], 64, "bf16", "f16", 4, stream=0) == mrr.MRR_EUNSUPPORTED
