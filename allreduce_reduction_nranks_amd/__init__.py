@@ -63,6 +63,8 @@ def load_library() -> ctypes.CDLL:
             "mrr_allreduce_packet_ex": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, i, i, vp], i),
             "mrr_packet_reduce": ([pp, vp, sz, i, i, i, u32, u32, u32, vp, vp], i),
             "mrr_allreduce": ([pp, pp, sz, i, i, i, vp, sz, vp, sz, u32, vp, vp], i),
+            "mrr_packet_rsag_scratch_bytes": ([sz, i, i], sz),
+            "mrr_allreduce_packet_rsag": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, i, i, vp], i),
             "mrr_pack": ([vp, vp, sz, u32, vp], i),
             "mrr_unpack": ([vp, vp, sz, vp], i),
             "mrr_fp8b15_to_f16": ([vp, vp, sz, vp], i),
@@ -177,6 +179,19 @@ def mrr_allreduce_packet_ex(inputs, outputs, scratch, scratch_bytes, flags, coun
                             nranks, max_spins, dev_err=None, blocks_per_rank=0, threads=0,
                             stream=None) -> int:
     return load_library().mrr_allreduce_packet_ex(
+        _ptrs(inputs), _ptrs(outputs), _ptr(scratch), scratch_bytes, _ptr(flags), count,
+        _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), blocks_per_rank, threads,
+        _stream(stream))
+
+
+def mrr_packet_rsag_scratch_bytes(count, dtype, nranks) -> int:
+    return load_library().mrr_packet_rsag_scratch_bytes(count, _dt(dtype), nranks)
+
+
+def mrr_allreduce_packet_rsag(inputs, outputs, scratch, scratch_bytes, flags, count, dtype, accum,
+                              nranks, max_spins, dev_err=None, blocks_per_rank=0, threads=0,
+                              stream=None) -> int:
+    return load_library().mrr_allreduce_packet_rsag(
         _ptrs(inputs), _ptrs(outputs), _ptr(scratch), scratch_bytes, _ptr(flags), count,
         _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), blocks_per_rank, threads,
         _stream(stream))

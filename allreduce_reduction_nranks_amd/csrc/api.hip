@@ -178,17 +178,15 @@ size_t mrr_packet_flag_bytes(int nranks) {
   return nranks <= 0 ? 0 : (size_t)nranks * MRR_PKT_FLAG_SLOTS * sizeof(uint32_t);
 }
 
-mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outputs, void* scratch,
-                                   size_t scratch_bytes, uint32_t* flags, size_t count,
-                                   mrr_dtype dtype, mrr_dtype accum, int nranks,
-                                   uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
-                                   int threads, void* stream) {
-  static const char* fn = "mrr_allreduce_packet";
+// Argument checks shared by the packet allreduce entry points; everything
+// here runs before any HIP call.
+static mrr_status packet_checks(const char* fn, const void* const* inputs, void* const* outputs,
+                                void* scratch, size_t scratch_bytes, size_t scratch_need,
+                                uint32_t* flags, size_t count, int t, int tacc, int nranks,
+                                int blocks_per_rank, int threads) {
   if (!valid_nranks(nranks)) return refuse(MRR_EUNSUPPORTED, fn, "nranks not in {2,4,8,16,32}");
   if (!inputs || !outputs || !scratch || !flags)
     return refuse(MRR_EINVAL, fn, "null pointer argument");
-  const int t = (int)dtype;
-  const int tacc = accum == MRR_AUTO ? t : (int)accum;
   if (!tsize(t) || !packet_supported(nranks, t, tacc))
     return refuse(MRR_EUNSUPPORTED, fn, "type combination");
   if (threads != 0 && (threads < 64 || threads > packet_max_threads() || threads % 64 != 0))
@@ -207,9 +205,8 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   const size_t nbytes = count * e;
   if (bad_overlap(inputs, nbytes, outputs, nbytes, nranks))
     return refuse(MRR_EOVERLAP, fn, "output overlaps another buffer");
-  const size_t need = mrr_packet_scratch_bytes(count, dtype, nranks);
-  if (scratch_bytes < need) return refuse(MRR_ESCRATCH, fn, "scratch smaller than required");
-  const Range sr{(uintptr_t)scratch, (uintptr_t)scratch + need};
+  if (scratch_bytes < scratch_need) return refuse(MRR_ESCRATCH, fn, "scratch smaller than required");
+  const Range sr{(uintptr_t)scratch, (uintptr_t)scratch + scratch_need};
   const Range fr{(uintptr_t)flags, (uintptr_t)flags + mrr_packet_flag_bytes(nranks)};
   if (overlaps(sr, fr)) return refuse(MRR_EOVERLAP, fn, "scratch overlaps flags");
   for (int r = 0; r < nranks; ++r) {
@@ -218,27 +215,48 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
     if (overlaps(sr, ir) || overlaps(sr, orr) || overlaps(fr, ir) || overlaps(fr, orr))
       return refuse(MRR_EOVERLAP, fn, "scratch/flags overlap a data buffer");
   }
+  return MRR_OK;
+}
 
-  const uint64_t npkt = (nbytes + 3) / 4;
-  const int T = threads ? threads : 64;
-  int B = blocks_per_rank;
-  // Geometry needs the device: how many workgroups fit at once.
-  const void* kernel = packet_allpair_kernel(nranks, t, tacc);
-  const int resident = max_resident_blocks(kernel, T);
+// Blocks per rank: the caller's, or one poll round per lane over `units`
+// words, capped by the workgroups the GPU holds at once and by the flag slots.
+static mrr_status packet_geometry(const char* fn, const void* kernel, int nranks, uint64_t units,
+                                  int threads, int blocks_per_rank, int* B) {
+  const int resident = max_resident_blocks(kernel, threads);
   if (resident <= 0) return hip_status(hipErrorInvalidDevice, fn);
   const int max_b = resident / nranks;
-  if (B == 0) {
-    // One poll round per lane when the GPU can hold that many workgroups:
-    // every round costs a memory round trip, and more workgroups spread the
-    // sends and polls over more CUs.
-    const uint64_t per_block = (uint64_t)T * packet_batch(nranks);
-    const uint64_t want = (npkt + per_block - 1) / per_block;
-    B = (int)(want < 1 ? 1 : (want > (uint64_t)MRR_PKT_FLAG_SLOTS ? MRR_PKT_FLAG_SLOTS : want));
-    if (B > max_b) B = max_b;
+  int b = blocks_per_rank;
+  if (b == 0) {
+    const uint64_t per_block = (uint64_t)threads * packet_batch(nranks);
+    const uint64_t want = (units + per_block - 1) / per_block;
+    b = (int)(want < 1 ? 1 : (want > (uint64_t)MRR_PKT_FLAG_SLOTS ? MRR_PKT_FLAG_SLOTS : want));
+    if (b > max_b) b = max_b;
   }
-  if (B < 1 || B > max_b)
+  if (b < 1 || b > max_b)
     return refuse(MRR_EINVAL, fn, "nranks * blocks_per_rank workgroups do not fit on the GPU at once");
+  *B = b;
+  return MRR_OK;
+}
 
+mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outputs, void* scratch,
+                                   size_t scratch_bytes, uint32_t* flags, size_t count,
+                                   mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                   uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
+                                   int threads, void* stream) {
+  static const char* fn = "mrr_allreduce_packet";
+  const int t = (int)dtype;
+  const int tacc = accum == MRR_AUTO ? t : (int)accum;
+  mrr_status st = packet_checks(fn, inputs, outputs, scratch, scratch_bytes,
+                                mrr_packet_scratch_bytes(count, dtype, nranks), flags, count, t,
+                                tacc, nranks, blocks_per_rank, threads);
+  if (st != MRR_OK || count == 0) return st;
+  const size_t nbytes = count * tsize(t);
+  const uint64_t npkt = (nbytes + 3) / 4;
+  const int T = threads ? threads : 64;
+  int B = 0;
+  st = packet_geometry(fn, packet_allpair_kernel(nranks, t, tacc), nranks, npkt, T,
+                       blocks_per_rank, &B);
+  if (st != MRR_OK) return st;
   PacketArgs a = {};
   for (int r = 0; r < nranks; ++r) {
     a.in[r] = inputs[r];
@@ -253,6 +271,55 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   a.nblocks = (uint32_t)B;
   a.max_spins = max_spins;
   return hip_status(launch_packet_allpair(a, nranks, t, tacc, T, (hipStream_t)stream), fn);
+}
+
+// Payload words per full chunk of the two-phase packet allreduce: the RS/AG
+// chunk C = roundup(ceil(count / N), 16 / e) elements, C * e / 4 words.
+static uint64_t rsag_chunk_words(size_t count, int e, int nranks) {
+  const uint64_t per = (count + (uint64_t)nranks - 1) / (uint64_t)nranks;
+  const uint64_t vw = 16 / (uint64_t)e;
+  return (per + vw - 1) / vw * vw * (uint64_t)e / 4;
+}
+
+size_t mrr_packet_rsag_scratch_bytes(size_t count, mrr_dtype dtype, int nranks) {
+  const int e = tsize((int)dtype);
+  if (!e || nranks <= 0) return 0;
+  return 2 * (size_t)nranks * (size_t)nranks * rsag_chunk_words(count, e, nranks) * 8;
+}
+
+mrr_status mrr_allreduce_packet_rsag(const void* const* inputs, void* const* outputs,
+                                     void* scratch, size_t scratch_bytes, uint32_t* flags,
+                                     size_t count, mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                     uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
+                                     int threads, void* stream) {
+  static const char* fn = "mrr_allreduce_packet_rsag";
+  const int t = (int)dtype;
+  const int tacc = accum == MRR_AUTO ? t : (int)accum;
+  mrr_status st = packet_checks(fn, inputs, outputs, scratch, scratch_bytes,
+                                mrr_packet_rsag_scratch_bytes(count, dtype, nranks), flags, count,
+                                t, tacc, nranks, blocks_per_rank, threads);
+  if (st != MRR_OK || count == 0) return st;
+  const int e = tsize(t);
+  const uint64_t cw = rsag_chunk_words(count, e, nranks);
+  const int T = threads ? threads : 64;
+  int B = 0;
+  st = packet_geometry(fn, packet_rsag_kernel(nranks, t, tacc), nranks, cw, T, blocks_per_rank, &B);
+  if (st != MRR_OK) return st;
+  PacketRsagArgs a = {};
+  for (int r = 0; r < nranks; ++r) {
+    a.in[r] = inputs[r];
+    a.out[r] = outputs[r];
+  }
+  a.scratch = (uint64_t*)scratch;
+  a.flags = flags;
+  a.dev_err = dev_err;
+  a.nbytes = count * (size_t)e;
+  a.nwords = (a.nbytes + 3) / 4;
+  a.cw = cw;
+  a.words_per_block = (cw + (uint64_t)B - 1) / (uint64_t)B;
+  a.nblocks = (uint32_t)B;
+  a.max_spins = max_spins;
+  return hip_status(launch_packet_rsag(a, nranks, t, tacc, T, (hipStream_t)stream), fn);
 }
 
 mrr_status mrr_allreduce_packet(const void* const* inputs, void* const* outputs, void* scratch,

@@ -69,6 +69,21 @@ struct PacketArgs {
   uint32_t max_spins;      // 0 = unbounded
 };
 
+// Two-phase (reduce-scatter then all-gather) packet allreduce.
+struct PacketRsagArgs {
+  const void* in[kMaxRanks];
+  void* out[kMaxRanks];
+  uint64_t* scratch;       // rs region [dst][src][cw], then ag region [dst][src][cw]
+  uint32_t* flags;         // [rank][kFlagSlots]
+  uint32_t* dev_err;       // may be null
+  uint64_t nbytes;         // payload bytes per rank
+  uint64_t nwords;         // payload words per rank
+  uint64_t cw;             // payload words per full chunk
+  uint64_t words_per_block;
+  uint32_t nblocks;        // B, blocks per rank
+  uint32_t max_spins;
+};
+
 struct PacketReduceArgs {
   const uint64_t* in[kMaxRanks];
   uint64_t* out;
@@ -89,6 +104,9 @@ hipError_t launch_packet_allpair(const PacketArgs& a, int nranks, int t, int tac
                                  hipStream_t stream);
 hipError_t launch_packet_reduce(const PacketReduceArgs& a, int nranks, int t, int tacc,
                                 hipStream_t stream);
+const void* packet_rsag_kernel(int nranks, int t, int tacc);
+hipError_t launch_packet_rsag(const PacketRsagArgs& a, int nranks, int t, int tacc, int threads,
+                              hipStream_t stream);
 hipError_t launch_pack(const void* src, uint64_t* pkts, size_t nbytes, uint32_t flag,
                        hipStream_t stream);
 hipError_t launch_unpack(const uint64_t* pkts, void* dst, size_t nbytes, hipStream_t stream);

@@ -190,6 +190,98 @@ __global__ void __launch_bounds__(kPktMaxThreads) packet_allpair_k(const PacketA
     my_flags[j] = F;
 }
 
+// Two-phase packet allreduce, workgroup (rank d, block b), slice b of every
+// chunk (chunk c = payload words [c * cw, min((c + 1) * cw, nwords))):
+//   1. reduce-scatter send: for every peer c, chunk c of rank d's input goes
+//      as packets to rs[c][d] (rank c's inbox for its chunk);
+//   2. reduce: poll rs[d][s] for every s != d, sum in rank order with rank
+//      d's own chunk d read from its input, write the result to output d and
+//      send it as packets to ag[p][d] for every peer p (all-gather send);
+//   3. all-gather receive: poll ag[d][s] for every s != d and write chunk s
+//      of output d.
+// Each lane handles the same slice word k in all three steps, so an input
+// word is read before the lane writes the output word at the same address
+// (in place works).  Phase 2 depends only on phase-1 packets, phase 3 only on
+// phase-2 packets, so with all N * B workgroups resident no wait is circular.
+template <int N, int T, int Acc>
+__global__ void __launch_bounds__(kPktMaxThreads) packet_rsag_k(const PacketRsagArgs a) {
+  const uint32_t d = blockIdx.x % N;
+  const uint32_t b = blockIdx.x / N;
+  uint32_t* const my_flags = a.flags + (uint64_t)d * kFlagSlots;
+  uint32_t F = my_flags[b] + 1u;
+  if (F == 0u) F = 1u;
+
+  const uint64_t cw = a.cw;
+  const uint64_t k_lo = (uint64_t)b * a.words_per_block;
+  const uint64_t k_hi = k_lo + a.words_per_block < cw ? k_lo + a.words_per_block : cw;
+  uint64_t* const rs = a.scratch;
+  uint64_t* const ag = a.scratch + (uint64_t)N * N * cw;
+  const void* src = a.in[d];
+  void* dst = a.out[d];
+
+  // 1. reduce-scatter send
+  for (uint64_t k = k_lo + threadIdx.x; k < k_hi; k += blockDim.x) {
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const uint64_t w = (uint64_t)c * cw + k;
+      if ((uint32_t)c != d && w < a.nwords)
+        st_pkt(rs + ((uint64_t)c * N + d) * cw + k, make_pkt(load_word(src, a.nbytes, w), F));
+    }
+  }
+
+  // 2. reduce chunk d and send it to every peer
+  const uint64_t wd0 = (uint64_t)d * cw;
+  bool ok = true;
+  for (uint64_t kb = k_lo; kb < k_hi && ok; kb += blockDim.x) {
+    uint64_t kp[1] = {kb + threadIdx.x};
+    const bool active = kp[0] < k_hi && wd0 + kp[0] < a.nwords;
+    uint32_t pending[1] = {active ? peer_mask<N>(d) : 0u};
+    uint32_t w[1][N];
+    ok = poll_batch<N, 1>(StridedSources{rs + (uint64_t)d * N * cw, cw}, kp, pending, w, F,
+                          a.max_spins);
+    if (!ok) {
+      report_timeout(a.dev_err);
+      break;
+    }
+    if (active) {
+      const uint64_t wd = wd0 + kp[0];
+      const uint32_t r = reduce_word<N, T, Acc>(w[0], d, load_word(src, a.nbytes, wd));
+      store_word(dst, a.nbytes, wd, r);
+      const uint64_t pkt = make_pkt(r, F);
+#pragma unroll
+      for (int p = 0; p < N; ++p)
+        if ((uint32_t)p != d) st_pkt(ag + ((uint64_t)p * N + d) * cw + kp[0], pkt);
+    }
+  }
+
+  // 3. all-gather receive
+  for (uint64_t kb = k_lo; kb < k_hi && ok; kb += blockDim.x) {
+    uint64_t kp[1] = {kb + threadIdx.x};
+    uint32_t pending[1] = {0u};
+    if (kp[0] < k_hi) {
+#pragma unroll
+      for (int s = 0; s < N; ++s)
+        if ((uint32_t)s != d && (uint64_t)s * cw + kp[0] < a.nwords) pending[0] |= 1u << s;
+    }
+    const uint32_t want = pending[0];
+    uint32_t w[1][N];
+    ok = poll_batch<N, 1>(StridedSources{ag + (uint64_t)d * N * cw, cw}, kp, pending, w, F,
+                          a.max_spins);
+    if (!ok) {
+      report_timeout(a.dev_err);
+      break;
+    }
+#pragma unroll
+    for (int s = 0; s < N; ++s)
+      if (want & (1u << s)) store_word(dst, a.nbytes, (uint64_t)s * cw + kp[0], w[0][s]);
+  }
+
+  __syncthreads();
+  for (uint32_t j = b + threadIdx.x * a.nblocks; j < (uint32_t)kFlagSlots;
+       j += blockDim.x * a.nblocks)
+    my_flags[j] = F;
+}
+
 // Receive step alone: packets from N producers outside the launch.
 template <int N, int T, int Acc>
 __global__ void __launch_bounds__(256) packet_reduce_k(const PacketReduceArgs a) {
@@ -284,6 +376,31 @@ hipError_t launch_packet_reduce(const PacketReduceArgs& a, int nranks, int t, in
 #define MRR_K(N, T, A)                                                               \
   if (nranks == N && t == T && tacc == A) {                                          \
     hipLaunchKernelGGL((packet_reduce_k<N, T, A>), grid, block, 0, stream, a);       \
+    return hipGetLastError();                                                        \
+  }
+#define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
+  MRR_PKT_PAIRS(MRR_ALLN)
+#undef MRR_ALLN
+#undef MRR_K
+  return hipErrorInvalidValue;
+}
+
+const void* packet_rsag_kernel(int nranks, int t, int tacc) {
+#define MRR_K(N, T, A) \
+  if (nranks == N && t == T && tacc == A) return (const void*)&packet_rsag_k<N, T, A>;
+#define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
+  MRR_PKT_PAIRS(MRR_ALLN)
+#undef MRR_ALLN
+#undef MRR_K
+  return nullptr;
+}
+
+hipError_t launch_packet_rsag(const PacketRsagArgs& a, int nranks, int t, int tacc, int threads,
+                              hipStream_t stream) {
+  const dim3 grid((uint32_t)nranks * a.nblocks), block((uint32_t)threads);
+#define MRR_K(N, T, A)                                                               \
+  if (nranks == N && t == T && tacc == A) {                                          \
+    hipLaunchKernelGGL((packet_rsag_k<N, T, A>), grid, block, 0, stream, a);         \
     return hipGetLastError();                                                        \
   }
 #define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)

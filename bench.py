@@ -230,14 +230,17 @@ def bench_packet(args, torch, mrr, synth):
     count = args.size * 1024 // 2
     ins = [x.to("cuda") for x in synth.rank_inputs("uniform", t, n, count, args.seed0)]
     outs = [torch.empty(count, dtype=torch.float16, device="cuda") for _ in range(n)]
-    sbytes = mrr.mrr_packet_scratch_bytes(count, t, n)
+    two_phase = args.algo == "rsag"
+    sbytes = (mrr.mrr_packet_rsag_scratch_bytes if two_phase else mrr.mrr_packet_scratch_bytes)(
+        count, t, n)
     scratch = torch.zeros(sbytes // 8, dtype=torch.int64, device="cuda")
     flags = torch.zeros(n * mrr.PKT_FLAG_SLOTS, dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    entry = mrr.mrr_allreduce_packet_rsag if two_phase else mrr.mrr_allreduce_packet_ex
 
     def step():
-        st = mrr.mrr_allreduce_packet_ex(ins, outs, scratch, sbytes, flags, count, t, "f32", n,
-                                         4_000_000, err, args.blocks, args.threads)
+        st = entry(ins, outs, scratch, sbytes, flags, count, t, "f32", n, 4_000_000, err,
+                   args.blocks, args.threads)
         if st != mrr.MRR_OK:
             raise mrr.MrrError(st)
 
@@ -245,13 +248,17 @@ def bench_packet(args, torch, mrr, synth):
     if int(err.item()) != 0:
         raise RuntimeError("packet poll timed out")
     S = count * 2
-    alg_bytes = 3 * n * S + 4 * n * (n - 1) * S
+    # allpair: send reads NS, packets 2N(N-1)S written and read, own input NS, outputs NS.
+    # two-phase: input NS; rs packets 2(N-1)S written and read; own chunk S; outputs NS;
+    # ag packets 2(N-1)S written and read.
+    alg_bytes = (3 * n * S + 8 * (n - 1) * S) if two_phase else (3 * n * S + 4 * n * (n - 1) * S)
+    name = "two-phase (RS + AG) packet" if two_phase else "LL-packet allpair"
     return {
-        "metric": "LL-packet allpair allreduce latency", "value": round(kern_ms * 1e3, 3),
+        "metric": "%s allreduce latency" % name, "value": round(kern_ms * 1e3, 3),
         "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall_ms, 5), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic ~U(-1,1)",
-        "config": {"workload": "LL-packet allpair allreduce, 8 ranks x %d KiB f16" % args.size,
+        "config": {"workload": "%s allreduce, 8 ranks x %d KiB f16" % (name, args.size),
                    "nranks": n, "bytes_per_rank": S, "blocks_per_rank": args.blocks,
                    "threads": args.threads, "algorithmic_bytes_per_call": alg_bytes,
                    "algorithmic_gbps": round(alg_bytes / (kern_ms * 1e-3) / 1e9, 2)},
@@ -268,6 +275,8 @@ def main():
     ap.add_argument("--nranks", type=int, default=8, help="c5: rank count")
     ap.add_argument("--out", default="f16", choices=["f16", "fp8", "f32"], help="c4: output type")
     ap.add_argument("--size", type=int, default=1024, help="c3 / custom: KiB per rank")
+    ap.add_argument("--algo", default="allpair", choices=["allpair", "rsag"],
+                    help="c3: allpair packets or the two-phase (RS + AG) packet variant")
     ap.add_argument("--blocks", type=int, default=0, help="c3: blocks per rank (0 = auto)")
     ap.add_argument("--threads", type=int, default=0, help="c3: threads (0 = auto)")
     ap.add_argument("--seed0", type=int, default=0)

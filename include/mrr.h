@@ -188,6 +188,35 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
                                    int threads, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Two-phase packet allreduce: reduce-scatter then all-gather, both in LL
+ * packets (the "packet" allreduce the commit log lists beside allpair, in
+ * the entry adding accumDtype; its structure is not on the pages, so this is
+ * the RS/AG partition carried by packets).  The index space is split as for
+ * RS/AG: chunk c = elements [c*C, (c+1)*C), C = roundup(ceil(count/N),
+ * 16/elem_size), i.e. cw = C*elem_size/4 payload words per chunk.
+ *   1. rank d sends chunk c of its input to rank c: rs[c][d][k] (c != d);
+ *   2. rank c waits for rs[c][s] (s != c), sums chunk c in rank order with
+ *      its own chunk read from its input, writes it to outputs[c] and sends
+ *      it to every peer: ag[p][c][k] (p != c);
+ *   3. rank p waits for ag[p][s] (s != p) and writes chunk s of outputs[p].
+ * Every packet carries the call's flag F (same flag contract, flag buffer
+ * and time-out behaviour as mrr_allreduce_packet; one flag buffer may serve
+ * both packet entry points).  Per rank it moves about 10*S bytes against
+ * (3 + 4(N-1))*S for allpair.
+ * scratch: 8-byte aligned, mrr_packet_rsag_scratch_bytes() bytes: the rs
+ *   region then the ag region, each [dst][src][cw] uint64 packets.  Zero it
+ *   once before first use.
+ * Other arguments and errors as mrr_allreduce_packet_ex.
+ * ------------------------------------------------------------------------ */
+size_t mrr_packet_rsag_scratch_bytes(size_t count, mrr_dtype dtype, int nranks);
+
+mrr_status mrr_allreduce_packet_rsag(const void* const* inputs, void* const* outputs,
+                                     void* scratch, size_t scratch_bytes, uint32_t* flags,
+                                     size_t count, mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                     uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
+                                     int threads, void* stream);
+
+/* --------------------------------------------------------------------------
  * One-call allreduce with algorithm selection ("Support 2 ranks in
  * AllreduceRsAgZeroCopy", section "why": selectors pick RS/AG zero-copy above
  * a message size and packets below it; section "what changed": rank counts

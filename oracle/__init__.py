@@ -68,6 +68,9 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_allreduce_packet.restype = i
     L.orc_packet_reduce.argtypes = [ctypes.POINTER(vp), vp, sz, i, i, i, u32, u32]
     L.orc_packet_reduce.restype = i
+    L.orc_allreduce_packet_rsag.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz,
+                                            i, i, i, u32]
+    L.orc_allreduce_packet_rsag.restype = i
     return L
 
 
@@ -198,6 +201,26 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected types")
         return scratch, outs[0]
+
+    def allreduce_packet_rsag(self, inputs, t: str, accum: str, flag: int):
+        """Expected (rs, ag, output) after one two-phase packet allreduce with
+        flag F: rs and ag have shape (N, N, cw) indexed [dst][src][word];
+        slots the call does not write are zero here."""
+        accum = _accum(t, accum)
+        ins = [_bits(a, t) for a in inputs]
+        n = len(ins)
+        count = ins[0].size
+        e = ELEM_SIZE[t]
+        per = -(-count // n)
+        chunk = -(-per // (16 // e)) * (16 // e)
+        cw = chunk * e // 4
+        scratch = np.zeros((2, n, n, cw), dtype=np.uint64)
+        outs = [np.empty(count, dtype=NP_BITS[t]) for _ in ins]
+        rc = self.L.orc_allreduce_packet_rsag(_ptr_array(ins), _ptr_array(outs), _ptr(scratch),
+                                              count, TYPE_IDS[t], TYPE_IDS[accum], n, flag)
+        if rc != 0:
+            raise ValueError("oracle rejected types")
+        return scratch[0], scratch[1], outs[0]
 
     def packet_reduce(self, in_pkts, t: str, accum: str, flag_in: int, flag_out: int):
         """Receive step alone.  Returns the output packets, or None when some input

@@ -343,6 +343,46 @@ int orc_allreduce_packet(const void* const* inputs, void* const* outputs,
   return orc_allreduce(inputs, outputs, count, t, tacc, t, nranks, nranks);
 }
 
+/* Two-phase packet allreduce (the "packet" variant: reduce-scatter then
+ * all-gather, both in packets) with flag F.  The index space is split into N
+ * chunks of C = roundup(ceil(count/N), 16/e) elements, i.e. cw = C*e/4
+ * payload words; chunk c's words are k = 0 .. words(c)-1 where words(c) is
+ * what remains of ceil(count*e/4) after c*cw (none for an empty chunk).
+ * Expected state after the call, scratch = two regions of N*N*cw packets:
+ *   phase 1: rs[(c*N + d)*cw + k] = pack(word c*cw + k of in[d], F), c != d
+ *   phase 2: ag[(p*N + c)*cw + k] = pack(word c*cw + k of the sum, F), p != c
+ * (other slots untouched), and every output equals orc_allreduce's. */
+int orc_allreduce_packet_rsag(const void* const* inputs, void* const* outputs,
+                              uint64_t* scratch, size_t count, int t, int tacc, int nranks,
+                              uint32_t flag) {
+  build_tables();
+  int e = orc_size(t);
+  if (!e || !orc_size(tacc) || nranks < 1) return -1;
+  size_t nbytes = count * (size_t)e, nwords = (nbytes + 3) / 4;
+  size_t per = (count + (size_t)nranks - 1) / (size_t)nranks;
+  size_t vw = 16 / (size_t)e;
+  size_t chunk = (per + vw - 1) / vw * vw;
+  size_t cw = chunk * (size_t)e / 4;
+  int rc = orc_allreduce(inputs, outputs, count, t, tacc, t, nranks, nranks);
+  if (rc) return rc;
+  uint64_t* rs = scratch;
+  uint64_t* ag = scratch + (size_t)nranks * nranks * cw;
+  for (int c = 0; c < nranks; ++c) {
+    for (size_t k = 0; k < cw; ++k) {
+      size_t w = (size_t)c * cw + k;
+      if (w >= nwords) break;
+      for (int d = 0; d < nranks; ++d) {
+        if (d == c) continue;
+        rs[((size_t)c * nranks + d) * cw + k] =
+            make_packet(word_at((const uint8_t*)inputs[d], nbytes, w), flag);
+        ag[((size_t)d * nranks + c) * cw + k] =
+            make_packet(word_at((const uint8_t*)outputs[0], nbytes, w), flag);
+      }
+    }
+  }
+  return 0;
+}
+
 /* Receive step alone: every input packet must carry flag_in (else the call
  * would wait forever; returns -2 without writing).  Each payload word holds
  * 4/e elements, summed over ranks in order with accumulation tacc, rounded to

@@ -219,3 +219,18 @@ def test_allreduce_dispatch_checks(lib):
     # the RS/AG entry itself keeps the pages' rank-count contract
     assert rsag(3, ins=ins[:3], outs=outs[:3]) == mrr.MRR_EUNSUPPORTED
     assert mrr.mrr_allreduce(ins[:4], outs[:4], 64, "bf16", "f16", 4, stream=0) == mrr.MRR_EUNSUPPORTED
+
+
+def test_packet_rsag_sizes_and_checks(lib):
+    # chunk C = roundup(ceil(count / N), 16 / e) elements, cw = C * e / 4 words, 2 regions
+    assert mrr.mrr_packet_rsag_scratch_bytes(1000, "f16", 8) == 2 * 8 * 8 * (128 * 2 // 4) * 8
+    assert mrr.mrr_packet_rsag_scratch_bytes(5, "f16", 8) == 2 * 8 * 8 * 4 * 8
+    assert mrr.mrr_packet_rsag_scratch_bytes(1023, "fp8", 4) == 2 * 4 * 4 * (256 // 4) * 8
+    ins = [fake(r) for r in range(8)]
+    outs = [fake(64 + r) for r in range(8)]
+    need = mrr.mrr_packet_rsag_scratch_bytes(4096, "f16", 8)
+    f = mrr.mrr_allreduce_packet_rsag
+    assert f(ins, outs, fake(200), need - 8, fake(300), 4096, "f16", "f32", 8, 10, 0, 0, 0, 0) == mrr.MRR_ESCRATCH
+    assert f(ins[:3], outs[:3], fake(200), need, fake(300), 4096, "f16", "f32", 3, 10, 0, 0, 0, 0) == mrr.MRR_EUNSUPPORTED
+    assert f(ins, outs, fake(200), need, fake(300), 4096, "f16", "f32", 8, 10, 0, 0, 96, 0) == mrr.MRR_EINVAL
+    assert f(ins, outs, fake(200), need, fake(300), 0, "f16", "f32", 8, 10, 0, 0, 0, 0) == mrr.MRR_OK

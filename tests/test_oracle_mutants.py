@@ -50,6 +50,10 @@ MUTANTS = [
      "uint32_t byte = at < nbytes ? src[at] : 0xFF;"),
     ("scratch indexed [src][dst]", "((size_t)d * nranks + s) * npkt;",
      "((size_t)s * nranks + d) * npkt;"),
+    ("two-phase scratch indexed [src][dst]", "rs[((size_t)c * nranks + d) * cw + k] =",
+     "rs[((size_t)d * nranks + c) * cw + k] ="),
+    ("two-phase all-gather of the input", "make_packet(word_at((const uint8_t*)outputs[0], nbytes, w), flag);",
+     "make_packet(word_at((const uint8_t*)inputs[c], nbytes, w), flag);"),
 ]
 
 
@@ -75,6 +79,7 @@ def _checks():
         pins.test_pack_layout_worked_example,
         pins.test_pack_unpack_roundtrip,
         lambda o: pins.test_allreduce_packet_expectation(o, "f16", 1001),
+        lambda o: pins.test_packet_rsag_expectation(o, "f16", 1001, 4),
     ]
 
 

@@ -517,3 +517,35 @@ def test_packet_reduce(orc):
     pk[3] = pk[3].copy()
     pk[3][17] = (pk[3][17] & np.uint64(0xFFFFFFFF)) | (np.uint64(2) << np.uint64(32))
     assert orc.packet_reduce(pk, "f16", "f32", 3, 4) is None
+
+
+@pytest.mark.parametrize("t,count,nranks", [("f16", 1001, 4), ("fp8", 1023, 8), ("f32", 5, 8),
+                                            ("bf16", 64, 2)])
+def test_packet_rsag_expectation(orc, t, count, nranks):
+    """Two-phase packet allreduce: chunk c of rank d's input goes to rank c
+    (reduce-scatter), chunk c of the sum goes from rank c to everyone
+    (all-gather).  Built here from numpy slicing and the pinned pack()."""
+    import synth
+    if t == "fp8":
+        xs = [_fp8_codes(count, 750 + r) for r in range(nranks)]
+    else:
+        xs = [synth.to_bits_numpy(synth.uniform(t, count, 750 + r)) for r in range(nranks)]
+    rs, ag, out = orc.allreduce_packet_rsag(xs, t, "f32", 5)
+    assert np.array_equal(out, orc.allreduce(xs, t, "f32"))
+    e = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[t]
+    cw = rs.shape[2]
+    chunk_bytes = cw * 4
+    assert chunk_bytes % 16 == 0 and chunk_bytes >= -(-count // nranks) * e
+    for c in range(nranks):
+        lo = c * chunk_bytes
+        for d in range(nranks):
+            if c == d:
+                assert not rs[c, d].any() and not ag[d, c].any()
+                continue
+            src = xs[d].view(np.uint8)[lo:lo + chunk_bytes]
+            want = orc.pack(src, 5) if src.size else np.zeros(0, np.uint64)
+            assert np.array_equal(rs[c, d, :want.size], want)
+            assert not rs[c, d, want.size:].any()
+            red = out.view(np.uint8)[lo:lo + chunk_bytes]
+            want = orc.pack(red, 5) if red.size else np.zeros(0, np.uint64)
+            assert np.array_equal(ag[d, c, :want.size], want)
