@@ -25,9 +25,10 @@ MRR_OK, MRR_EINVAL, MRR_EUNSUPPORTED, MRR_EALIGN, MRR_EOVERLAP, MRR_ESCRATCH, \
 STATUS_NAMES = ["MRR_OK", "MRR_EINVAL", "MRR_EUNSUPPORTED", "MRR_EALIGN", "MRR_EOVERLAP",
                 "MRR_ESCRATCH", "MRR_ETIMEDOUT", "MRR_EHIP"]
 # mrr_dtype
-MRR_AUTO, MRR_F32, MRR_F16, MRR_BF16, MRR_FP8_E4M3B15 = range(5)
+MRR_AUTO, MRR_F32, MRR_F16, MRR_BF16, MRR_FP8_E4M3B15, MRR_FP8_E4M3FN = range(6)
 DTYPES = {"auto": MRR_AUTO, "f32": MRR_F32, "f16": MRR_F16, "bf16": MRR_BF16,
-          "fp8": MRR_FP8_E4M3B15, "fp8_e4m3b15": MRR_FP8_E4M3B15}
+          "fp8": MRR_FP8_E4M3B15, "fp8_e4m3b15": MRR_FP8_E4M3B15,
+          "fp8fn": MRR_FP8_E4M3FN, "fp8_e4m3fn": MRR_FP8_E4M3FN}
 MAX_RANKS = 32
 PKT_FLAG_SLOTS = 1024
 
@@ -138,7 +139,8 @@ def alloc_rank_buffers(nranks: int, count: int, dtype, device=None):
     import torch
     tdt = dtype if isinstance(dtype, torch.dtype) else \
         {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-         "fp8": torch.uint8, "fp8_e4m3b15": torch.uint8}[dtype]
+         "fp8": torch.uint8, "fp8_e4m3b15": torch.uint8, "fp8fn": torch.uint8,
+         "fp8_e4m3fn": torch.uint8}[dtype]
     esize = torch.empty((), dtype=tdt).element_size()
     nbytes = count * esize
     pitch = mrr_rank_buffer_pitch(nbytes, nranks)

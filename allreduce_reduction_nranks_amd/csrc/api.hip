@@ -30,6 +30,7 @@ static int tsize(int t) {
     case kF16: return 2;
     case kBF16: return 2;
     case kFP8: return 1;
+    case kFP8FN: return 1;
     default: return 0;
   }
 }

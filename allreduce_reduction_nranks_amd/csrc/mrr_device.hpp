@@ -16,13 +16,17 @@
 
 namespace mrr {
 
-enum : int { kF32 = 1, kF16 = 2, kBF16 = 3, kFP8 = 4 };
+enum : int { kF32 = 1, kF16 = 2, kBF16 = 3, kFP8 = 4, kFP8FN = 5 };
+
+// 1-byte floating-point types.
+constexpr bool is_fp8(int t) { return t == kFP8 || t == kFP8FN; }
 
 template <int T> struct Ty;
 template <> struct Ty<kF32> { static constexpr int size = 4; };
 template <> struct Ty<kF16> { static constexpr int size = 2; };
 template <> struct Ty<kBF16> { static constexpr int size = 2; };
 template <> struct Ty<kFP8> { static constexpr int size = 1; };
+template <> struct Ty<kFP8FN> { static constexpr int size = 1; };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -115,6 +119,32 @@ __device__ __forceinline__ uint32_t f16_to_fp8(uint32_t h) {
   return sign | q;
 }
 
+// OCP FP8 E4M3FN (bias 7, largest finite 448, S.1111.111 NaN, no infinity)
+// -> f32: the gfx950 convert is exact for every code.
+__device__ __forceinline__ float fp8fn_to_f32(uint32_t c) {
+  const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+  return v.x;
+}
+
+// Two f32 -> two OCP FP8 E4M3FN codes in bytes 2*HI and 2*HI+1 of `old`:
+// one round-to-nearest-even each (the hardware convert), saturating at +-448
+// (also for +-inf); NaN gives 0x7F with the input's sign.
+template <bool HI>
+__device__ __forceinline__ uint32_t encode2_fp8fn(float a, float b, uint32_t old) {
+  const float ya = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float yb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, (int)old, HI);
+  constexpr int sh = HI ? 16 : 0;
+  if (a != a) w = (w & ~(0xFFu << sh)) | ((((__float_as_uint(a) >> 24) & 0x80u) | 0x7Fu) << sh);
+  if (b != b)
+    w = (w & ~(0xFFu << (sh + 8))) | ((((__float_as_uint(b) >> 24) & 0x80u) | 0x7Fu) << (sh + 8));
+  return w;
+}
+
+__device__ __forceinline__ uint32_t f32_to_fp8fn(float f) {
+  return encode2_fp8fn<false>(f, f, 0u) & 0xFFu;
+}
+
 // ---------------------------------------------------------------------------
 // Generic element access by type id (T)
 // ---------------------------------------------------------------------------
@@ -123,12 +153,14 @@ template <> __device__ __forceinline__ float to_f32<kF32>(uint32_t b) { return _
 template <> __device__ __forceinline__ float to_f32<kF16>(uint32_t b) { return f16_to_f32(b); }
 template <> __device__ __forceinline__ float to_f32<kBF16>(uint32_t b) { return bf16_to_f32(b); }
 template <> __device__ __forceinline__ float to_f32<kFP8>(uint32_t b) { return fp8_to_f32(b); }
+template <> __device__ __forceinline__ float to_f32<kFP8FN>(uint32_t b) { return fp8fn_to_f32(b); }
 
 template <int T> __device__ __forceinline__ uint32_t from_f32(float f);
 template <> __device__ __forceinline__ uint32_t from_f32<kF32>(float f) { return __float_as_uint(f); }
 template <> __device__ __forceinline__ uint32_t from_f32<kF16>(float f) { return f32_to_f16(f); }
 template <> __device__ __forceinline__ uint32_t from_f32<kBF16>(float f) { return f32_to_bf16(f); }
 template <> __device__ __forceinline__ uint32_t from_f32<kFP8>(float f) { return f32_to_fp8(f); }
+template <> __device__ __forceinline__ uint32_t from_f32<kFP8FN>(float f) { return f32_to_fp8fn(f); }
 
 // Rounds an f32 partial sum to the accumulator type.  The f32 add before it is
 // itself rounded, but f32 carries at least 2p+2 bits for p = 11 (f16), 8 (bf16)
@@ -142,6 +174,9 @@ template <> __device__ __forceinline__ float round_acc<kBF16>(float s) {
 }
 template <> __device__ __forceinline__ float round_acc<kFP8>(float s) {
   return fp8_to_f32(f32_to_fp8(s));
+}
+template <> __device__ __forceinline__ float round_acc<kFP8FN>(float s) {
+  return s != s ? s : fp8fn_to_f32(f32_to_fp8fn(s));
 }
 
 // Element i of a buffer of type T, widened to f32.
@@ -229,6 +264,13 @@ template <int T> __device__ __forceinline__ void decode_word(uint32_t w, float* 
   } else if constexpr (T == kBF16) {
     x[0] = __uint_as_float(w << 16);
     x[1] = __uint_as_float(w & 0xFFFF0000u);
+  } else if constexpr (T == kFP8FN) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    x[0] = lo.x;
+    x[1] = lo.y;
+    x[2] = hi.x;
+    x[3] = hi.y;
   } else {
 #pragma unroll
     for (int b = 0; b < 4; ++b) x[b] = fp8_to_f32((w >> (8 * b)) & 0xFFu);
@@ -321,12 +363,18 @@ template <int T> __device__ __forceinline__ u32x4 encode16(const float* x) {
       p.y = x[2 * j + 1];
       v[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
     }
+  } else if constexpr (T == kFP8FN) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = encode2_fp8fn<false>(x[4 * j], x[4 * j + 1], 0u);
+      v[j] = encode2_fp8fn<true>(x[4 * j + 2], x[4 * j + 3], w);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t w = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) w |= f32_to_fp8(x[4 * j + b]) << (8 * b);
+      for (int b = 0; b < 4; ++b) w |= from_f32<T>(x[4 * j + b]) << (8 * b);
       v[j] = w;
     }
   }

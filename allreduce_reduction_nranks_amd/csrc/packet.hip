@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(256) unpack_k(const uint64_t* pkts, void* dst,
 // (type, accumulator) pairs; the output type is the input type.
 #define MRR_PKT_PAIRS(X)                                                                  \
   X(kF32, kF32) X(kF16, kF32) X(kF16, kF16) X(kBF16, kF32) X(kBF16, kBF16) X(kFP8, kF32) \
-  X(kFP8, kF16) X(kFP8, kFP8)
+  X(kFP8, kF16) X(kFP8, kFP8) X(kFP8FN, kF32) X(kFP8FN, kF16) X(kFP8FN, kFP8FN)
 
 #define MRR_PKT_RANKS(X, T, A) X(2, T, A) X(4, T, A) X(8, T, A) X(16, T, A) X(32, T, A)
 

@@ -42,16 +42,17 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup
 // stayed near the best across buffer sizes rather than a formula.
 //   16-bit and 32-bit inputs: N=2 U=8 x2, N=4 U=4 x4, N=8 U=1 x6,
 //                             N=16 U=2 x2, N=32 U=1 x8 (workgroups per CU)
-//   FP8 inputs: U=4 for N=2, else 1, times 2 for f16 and 4 for f32 outputs
+//   FP8 inputs (E4M3B15 and OCP E4M3FN): U=4 for N=2, else 1, times 2 for
+//                             f16 and 4 for f32 outputs
 //                             (so a lane still loads 16 bytes per rank);
 //                             workgroups per CU: 4 (FP8 out), 3 (f16 out),
 //                             4 (f32 out).
 constexpr int rsag_unroll(int n, int tin, int tout) {
-  if (tin == kFP8) return (n == 2 ? 4 : 1) * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
+  if (is_fp8(tin)) return (n == 2 ? 4 : 1) * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
   return n == 2 ? 8 : n == 4 ? 4 : n == 16 ? 2 : 1;
 }
 constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
-  if (tin == kFP8) return tout == kF16 ? 3 : 4;
+  if (is_fp8(tin)) return tout == kF16 ? 3 : 4;
   return n == 2 ? 2 : n == 4 ? 4 : n == 8 ? 6 : n == 16 ? 2 : 8;
 }
 // Ranks whose vectors are loaded together before they are added: all of them
@@ -59,7 +60,7 @@ constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
 // an FP8 accumulator (16 values per vector and two decode paths make the
 // unrolled body large).
 constexpr int rsag_group(int n, int tin, int tacc) {
-  return (tin == kFP8 || tacc == kFP8) ? (n < 8 ? n : 8) : (n < 16 ? n : 16);
+  return (is_fp8(tin) || is_fp8(tacc)) ? (n < 8 ? n : 8) : (n < 16 ? n : 16);
 }
 
 template <int In, int Acc, int Out>
@@ -268,7 +269,9 @@ __global__ void __launch_bounds__(256) rsag_scalar_kernel(const RsagScalarArgs a
   X(kF32, kF32, kF32) X(kF16, kF32, kF16) X(kF16, kF16, kF16) X(kBF16, kF32, kBF16)      \
   X(kBF16, kBF16, kBF16) X(kFP8, kF32, kFP8) X(kFP8, kF32, kF16) X(kFP8, kF32, kF32)     \
   X(kFP8, kF16, kFP8) X(kFP8, kF16, kF16) X(kFP8, kF16, kF32) X(kFP8, kFP8, kFP8)        \
-  X(kFP8, kFP8, kF16) X(kFP8, kFP8, kF32)
+  X(kFP8, kFP8, kF16) X(kFP8, kFP8, kF32) X(kFP8FN, kF32, kFP8FN) X(kFP8FN, kF32, kF16)     \
+  X(kFP8FN, kF32, kF32) X(kFP8FN, kF16, kFP8FN) X(kFP8FN, kF16, kF16) X(kFP8FN, kF16, kF32) \
+  X(kFP8FN, kFP8FN, kFP8FN) X(kFP8FN, kFP8FN, kF16) X(kFP8FN, kFP8FN, kF32)
 
 static bool valid_nranks(int n) { return n == 2 || n == 4 || n == 8 || n == 16 || n == 32; }
 
@@ -284,8 +287,6 @@ bool rsag_types_supported(int tin, int tacc, int tout) {
 bool rsag_supported(int nranks, int tin, int tacc, int tout) {
   return valid_nranks(nranks) && rsag_types_supported(tin, tacc, tout);
 }
-
-static int type_size(int t) { return t == kF32 ? 4 : (t == kFP8 ? 1 : 2); }
 
 template <int In, int Acc, int Out>
 static void launch_vec_typed(int nranks, dim3 grid, const RsagArgs& a, hipStream_t s) {
@@ -305,26 +306,21 @@ static void launch_vec_typed(int nranks, dim3 grid, const RsagArgs& a, hipStream
 // The runtime-N kernel loads 16 bytes per lane per rank like the compiled
 // ones at N = 8; one unit per lane, 6 workgroups per CU.
 constexpr int rsag_any_unroll(int tin, int tout) {
-  return tin == kFP8 ? (tout == kF32 ? 4 : tout == kF16 ? 2 : 1) : 1;
+  return is_fp8(tin) ? (tout == kF32 ? 4 : tout == kF16 ? 2 : 1) : 1;
 }
 constexpr int kAnyWgPerCu = 6;
 
+// Plans and launches one type triple.  The chunk and unit geometry comes from
+// the same compile-time element sizes the kernels index with (Ty, Unit), so
+// the host plan and the kernel cannot disagree on how many elements a unit
+// or an input vector holds.
 template <int In, int Acc, int Out>
-static void launch_any_typed(dim3 grid, const RsagArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, rsag_any_unroll(In, Out)>), grid,
-                     dim3(kRsagThreads), 0, s, a);
-}
-
-template <int In, int Acc, int Out>
-static void launch_scalar_typed(dim3 grid, const RsagScalarArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rsag_scalar_kernel<In, Acc, Out>), grid, dim3(256), 0, s, a);
-}
-
-hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const* outputs,
-                       hipStream_t stream) {
+static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs,
+                                    void* const* outputs, hipStream_t stream) {
   const int n = p.nranks;
-  const uint64_t vw = 16 / type_size(p.tin);   // chunk granularity: 16-byte input vectors
-  const uint64_t ue = 16 / type_size(p.tout);  // elements per unit (16-byte output vector)
+  constexpr uint64_t vw = 16 / Ty<In>::size;  // chunk granularity: 16-byte input vectors
+  constexpr uint64_t ue = Unit<In, Out>::UE;  // elements per unit (16-byte output vector)
+  static_assert(vw % ue == 0, "a unit must divide an input vector");
   const uint64_t count = p.count;
   // Chunk width: ceil(count / N) rounded up to whole 16-byte input vectors.
   const uint64_t per = (count + n - 1) / n;
@@ -336,15 +332,15 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
       a.in[r] = inputs[r];
       a.out[r] = outputs[r];
     }
-    a.chunk_vecs = chunk_elems / ue;  // whole units: ue divides vw
+    a.chunk_vecs = chunk_elems / ue;
     a.total_vecs = count / ue;
     a.tail_begin = a.total_vecs * ue;
     const uint32_t tail = (uint32_t)(count - a.tail_begin);
-    const uint64_t tail_chunk = a.total_vecs / a.chunk_vecs;
+    const uint64_t tail_chunk = a.chunk_vecs ? a.total_vecs / a.chunk_vecs : 0;
     const bool any_n = !valid_nranks(n);
     a.nranks = (uint32_t)n;
     const uint64_t tile_vecs =
-        (uint64_t)kRsagThreads * (any_n ? rsag_any_unroll(p.tin, p.tout) : rsag_unroll(n, p.tin, p.tout));
+        (uint64_t)kRsagThreads * (any_n ? rsag_any_unroll(In, Out) : rsag_unroll(n, In, Out));
     a.tiles_per_chunk = (uint32_t)((a.chunk_vecs + tile_vecs - 1) / tile_vecs);
     uint32_t nchunks;
     if (p.rank < 0) {
@@ -357,8 +353,9 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
       a.tail_count = tail_chunk == (uint64_t)p.rank ? tail : 0;
     }
     a.launch_tiles = nchunks * a.tiles_per_chunk;
+    if (a.launch_tiles == 0 && a.tail_count == 0) return hipSuccess;
     // Persistent grid: wg_per_cu workgroups per CU (MRR_RSAG_WPC overrides).
-    int wpc = any_n ? kAnyWgPerCu : rsag_wg_per_cu(n, p.tin, p.tout);
+    int wpc = any_n ? kAnyWgPerCu : rsag_wg_per_cu(n, In, Out);
     static const int wpc_env = [] {
       const char* v = getenv("MRR_RSAG_WPC");
       return v ? atoi(v) : 0;
@@ -367,18 +364,13 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
     uint64_t blocks = (uint64_t)device_cu_count(-1) * (uint64_t)wpc;
     if (blocks == 0) blocks = 1024;
     if (blocks > a.launch_tiles) blocks = a.launch_tiles;
+    if (blocks == 0) blocks = 1;  // tail only
     const dim3 grid((uint32_t)blocks);
-    if (any_n) {
-#define MRR_DISPATCH(I, A, O) \
-  if (p.tin == I && p.tacc == A && p.tout == O) launch_any_typed<I, A, O>(grid, a, stream);
-      MRR_RSAG_TRIPLES(MRR_DISPATCH)
-#undef MRR_DISPATCH
-    } else {
-#define MRR_DISPATCH(I, A, O) \
-  if (p.tin == I && p.tacc == A && p.tout == O) launch_vec_typed<I, A, O>(n, grid, a, stream);
-      MRR_RSAG_TRIPLES(MRR_DISPATCH)
-#undef MRR_DISPATCH
-    }
+    if (any_n)
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, rsag_any_unroll(In, Out)>), grid,
+                         dim3(kRsagThreads), 0, stream, a);
+    else
+      launch_vec_typed<In, Acc, Out>(n, grid, a, stream);
   } else {
     RsagScalarArgs a = {};
     for (int r = 0; r < n; ++r) {
@@ -398,13 +390,19 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
     uint64_t blocks = (work + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     if (blocks == 0) return hipSuccess;
-    const dim3 grid((uint32_t)blocks);
-#define MRR_DISPATCH(I, A, O) \
-  if (p.tin == I && p.tacc == A && p.tout == O) launch_scalar_typed<I, A, O>(grid, a, stream);
-    MRR_RSAG_TRIPLES(MRR_DISPATCH)
-#undef MRR_DISPATCH
+    hipLaunchKernelGGL((rsag_scalar_kernel<In, Acc, Out>), dim3((uint32_t)blocks), dim3(256), 0,
+                       stream, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const* outputs,
+                       hipStream_t stream) {
+#define MRR_DISPATCH(I, A, O) \
+  if (p.tin == I && p.tacc == A && p.tout == O) return launch_rsag_typed<I, A, O>(p, inputs, outputs, stream);
+  MRR_RSAG_TRIPLES(MRR_DISPATCH)
+#undef MRR_DISPATCH
+  return hipErrorInvalidValue;  // callers check rsag_types_supported first
 }
 
 }  // namespace mrr

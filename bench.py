@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (and % of peak) for N-rank reduce at 64–256 MiB/rank"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 MiB = 1 << 20
-ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["allreduce_reduction_nranks_amd/csrc/rsag.hip",
                   "allreduce_reduction_nranks_amd/csrc/mrr_device.hpp",
@@ -132,8 +132,8 @@ def bench_rsag(args, torch, mrr, synth):
         tout, acc = t, "f32"
         kind = "normal"
     elif args.config == "c4":
-        n, t, per_rank = 8, "fp8", 32 * MiB
-        tout, acc = args.out, "f32"
+        n, t, per_rank = 8, ("fp8fn" if args.fp8 == "e4m3fn" else "fp8"), 32 * MiB
+        tout, acc = (t if args.out == "fp8" else args.out), "f32"
         kind = "fp8codes"
     elif args.config == "c5":
         n, t, per_rank = args.nranks, "bf16", 256 * MiB
@@ -141,8 +141,9 @@ def bench_rsag(args, torch, mrr, synth):
         kind = "normal"
     elif args.config == "custom":
         n, t, per_rank = args.nranks, args.dtype, args.size * 1024
-        tout, acc = (args.out if args.dtype == "fp8" else t), "f32"
-        kind = "fp8codes" if t == "fp8" else "normal"
+        fp8 = t in ("fp8", "fp8fn")
+        tout, acc = ((t if args.out == "fp8" else args.out) if fp8 else t), "f32"
+        kind = "fp8codes" if fp8 else "normal"
     else:
         n, t, per_rank = 8, "f16", 64 * MiB
         tout, acc = t, "f32"
@@ -189,15 +190,16 @@ def bench_rsag(args, torch, mrr, synth):
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     key = {"c1": "rsag_2x1MiB_bf16", "c2": "rsag_8x64MiB_f16",
-           "c4": "rsag_8x32MiB_fp8_to_%s" % tout, "c5": "rsag_%dx256MiB_bf16" % n,
+           "c4": "rsag_8x32MiB_%s_to_%s" % (t, tout), "c5": "rsag_%dx256MiB_bf16" % n,
            "custom": "rsag_%dx%dKiB_%s" % (n, args.size, t)}[args.config]
     traffic = measured_traffic(key)
     ceiling = copy_ceiling(torch, n * count * ESIZE[t]) if args.copy_ceiling else None
     workload = {"c1": "RS/AG allreduce, 2 ranks x 1 MiB bf16 ~N(0,1), fp32 accumulation",
                 "c2": "RS/AG zero-copy allreduce, 8 ranks x 64 MiB f16 ~N(0,1), fp32 accumulation, "
                       "reduced chunks written to all 8 outputs",
-                "c4": "RS/AG allreduce, 8 ranks x 32 MiB FP8 E4M3B15 finite codes, fp32 "
-                      "accumulation, %s outputs" % tout,
+                "c4": "RS/AG allreduce, 8 ranks x 32 MiB FP8 %s finite codes, fp32 "
+                      "accumulation, %s outputs"
+                      % ("E4M3B15" if t == "fp8" else "OCP E4M3FN", tout),
                 "c5": "RS/AG allreduce, %d ranks x 256 MiB bf16 ~N(0,1), fp32 accumulation" % n,
                 "custom": "RS/AG allreduce, %d ranks x %d KiB %s, fp32 accumulation, %s outputs"
                           % (n, args.size, t, tout)}[args.config]
@@ -271,9 +273,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "custom"])
-    ap.add_argument("--dtype", default="f16", choices=["f32", "f16", "bf16", "fp8"], help="custom: type")
+    ap.add_argument("--dtype", default="f16", choices=["f32", "f16", "bf16", "fp8", "fp8fn"],
+                    help="custom: type (fp8 = E4M3B15, fp8fn = OCP E4M3FN)")
     ap.add_argument("--nranks", type=int, default=8, help="c5: rank count")
-    ap.add_argument("--out", default="f16", choices=["f16", "fp8", "f32"], help="c4: output type")
+    ap.add_argument("--out", default="f16", choices=["f16", "fp8", "f32"],
+                    help="c4 / custom FP8: output type (fp8 = the input's FP8 format)")
+    ap.add_argument("--fp8", default="e4m3b15", choices=["e4m3b15", "e4m3fn"],
+                    help="c4: FP8 input format")
     ap.add_argument("--size", type=int, default=1024, help="c3 / custom: KiB per rank")
     ap.add_argument("--algo", default="allpair", choices=["allpair", "rsag"],
                     help="c3: allpair packets or the two-phase (RS + AG) packet variant")

@@ -44,8 +44,12 @@
  *     bfloat16, FP8 E4M3B15 as one byte (sign, 4-bit exponent with bias 15,
  *     3-bit mantissa; exponent 15 encodes inf (mantissa 0) and NaN).
  *   - Rounding is IEEE round-to-nearest-even everywhere.  f16 / bf16 overflow
- *     gives +-inf; FP8 E4M3B15 saturates to +-0.9375 (also from +-inf); NaN
- *     gives NaN (FP8: 0x7F with the input's sign).  Denormals are kept.
+ *     gives +-inf; FP8 E4M3B15 saturates to +-0.9375 and OCP FP8 E4M3FN to
+ *     +-448 (also from +-inf); NaN gives NaN (FP8: 0x7F with the input's
+ *     sign).  Denormals are kept.
+ *   - OCP FP8 E4M3FN (MRR_FP8_E4M3FN) is accepted wherever FP8 E4M3B15 is as
+ *     an input / accumulator / output type of the allreduce entry points
+ *     (the pages' benchmarks reduce fp8_e4m3fn data; PR #948, "why").
  */
 #ifndef MRR_H
 #define MRR_H
@@ -73,7 +77,8 @@ typedef enum mrr_dtype {
   MRR_F32 = 1,
   MRR_F16 = 2,
   MRR_BF16 = 3,
-  MRR_FP8_E4M3B15 = 4
+  MRR_FP8_E4M3B15 = 4,
+  MRR_FP8_E4M3FN = 5 /* OCP FP8 E4M3FN: bias 7, largest finite 448, 0x7F/0xFF NaN, no inf */
 } mrr_dtype;
 
 /* Packet / RS-AG crossover for mrr_allreduce, measured on one MI355X: 0.

@@ -7,7 +7,8 @@ its Python binding) never imports or calls it, and the two share no code.
 The arithmetic lives in ``mrr_oracle.c`` (plain C, table-driven rounding,
 sequential rank-order sums); this module only builds it with gcc and marshals
 numpy arrays through ctypes.  Values travel as raw bits: f32 as ``float32``,
-f16 and bf16 as ``uint16`` codes, FP8 E4M3B15 as ``uint8`` codes.
+f16 and bf16 as ``uint16`` codes, FP8 E4M3B15 ("fp8") and OCP FP8 E4M3FN
+("fp8fn") as ``uint8`` codes.
 
 What each function computes, and which passage it follows, is stated in the C
 source next to the function.  Parity status of every function is pinned by the
@@ -27,9 +28,10 @@ _SRC = os.path.join(_HERE, "mrr_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_mrr.so")
 
 # Type ids private to the oracle (mirrors the enum at the top of mrr_oracle.c).
-TYPE_IDS = {"f32": 1, "f16": 2, "bf16": 3, "fp8": 4}
-NP_BITS = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
-ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+TYPE_IDS = {"f32": 1, "f16": 2, "bf16": 3, "fp8": 4, "fp8fn": 5}
+NP_BITS = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8,
+           "fp8fn": np.uint8}
+ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
 
 _lock = threading.Lock()
 _lib = None

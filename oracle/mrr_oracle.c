@@ -22,6 +22,10 @@
  *   - Same entry: FP8 E4M3B15 has 4 exponent bits, 3 mantissa bits, bias 15,
  *     and its largest finite value is 0.9375.  Exponent field 15 therefore
  *     holds no finite value; it is read as IEEE-style inf (m=0) / NaN (m!=0).
+ *   - "Support 2 ranks in AllreduceRsAgZeroCopy", section "why": the pages
+ *     also reduce OCP fp8_e4m3fn data (4 exponent bits, bias 7, 3 mantissa
+ *     bits, no infinity, S.1111.111 = NaN, largest finite 448); its rounding
+ *     is taken to saturate like E4M3B15's.
  *   - MSCCL++ commit history, entry fixing allreduce_allpair_packet: each rank
  *     sends its data as low-latency packets to every peer, the receiver waits
  *     for the packet flag, reduces and writes back; the input buffer is never
@@ -46,7 +50,7 @@
 #include <string.h>
 
 /* ---- type ids, private to the oracle (the Python wrapper maps names) ---- */
-enum { ORC_F32 = 1, ORC_F16 = 2, ORC_BF16 = 3, ORC_FP8 = 4 };
+enum { ORC_F32 = 1, ORC_F16 = 2, ORC_BF16 = 3, ORC_FP8 = 4, ORC_FP8FN = 5 };
 
 static int orc_size(int t) {
   switch (t) {
@@ -54,6 +58,7 @@ static int orc_size(int t) {
     case ORC_F16: return 2;
     case ORC_BF16: return 2;
     case ORC_FP8: return 1;
+    case ORC_FP8FN: return 1;
     default: return 0;
   }
 }
@@ -95,6 +100,18 @@ static double fp8_value(uint8_t c) {
   return s ? -v : v;
 }
 
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 fraction bits; e=0 is
+ * subnormal (m/8 * 2^-6); no infinity; e=15 with m=7 is NaN, so the largest
+ * finite value is 2^8 * 1.75 = 448. */
+static double fp8fn_value(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 0xF, m = c & 0x7;
+  double v;
+  if (e == 0xF && m == 7) v = NAN;
+  else if (e == 0) v = ldexp((double)m / 8.0, -6);
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
 /* IEEE binary32 from its bits, by the same field definition. */
 static double f32_value(uint32_t c) {
   int s = c >> 31, e = (c >> 23) & 0xFF;
@@ -112,10 +129,12 @@ static double f32_value(uint32_t c) {
 #define F16_NFIN 0x7C00   /* codes 0x0000..0x7BFF are the finite >= 0 values */
 #define BF16_NFIN 0x7F80  /* codes 0x0000..0x7F7F */
 #define FP8_NFIN 0x78     /* codes 0x00..0x77 */
+#define FP8FN_NFIN 0x7F   /* codes 0x00..0x7E */
 
 static double f16_tab[F16_NFIN + 1];   /* + sentinel 2^16 standing for inf  */
 static double bf16_tab[BF16_NFIN + 1]; /* + sentinel 2^128 standing for inf */
 static double fp8_tab[FP8_NFIN];
+static double fp8fn_tab[FP8FN_NFIN];
 static int tabs_ready = 0;
 
 static void build_tables(void) {
@@ -125,6 +144,7 @@ static void build_tables(void) {
   for (int c = 0; c < BF16_NFIN; ++c) bf16_tab[c] = bf16_value((uint16_t)c);
   bf16_tab[BF16_NFIN] = ldexp(1.0, 128);
   for (int c = 0; c < FP8_NFIN; ++c) fp8_tab[c] = fp8_value((uint8_t)c);
+  for (int c = 0; c < FP8FN_NFIN; ++c) fp8fn_tab[c] = fp8fn_value((uint8_t)c);
   tabs_ready = 1;
 }
 
@@ -173,6 +193,16 @@ static uint8_t narrow_fp8(double x) {
   return s | (uint8_t)nearest_even(fp8_tab, FP8_NFIN, a);
 }
 
+/* Round-to-nearest-even into OCP FP8 E4M3FN, saturating at +-448 (also for
+ * +-inf); NaN gives 0x7F with the input's sign. */
+static uint8_t narrow_fp8fn(double x) {
+  if (isnan(x)) return (uint8_t)((signbit(x) ? 0x80 : 0) | 0x7F);
+  uint8_t s = signbit(x) ? 0x80 : 0;
+  double a = fabs(x);
+  if (a >= fp8fn_tab[FP8FN_NFIN - 1]) return s | (uint8_t)(FP8FN_NFIN - 1);
+  return s | (uint8_t)nearest_even(fp8fn_tab, FP8FN_NFIN, a);
+}
+
 /* Round-to-nearest-even into binary32: the C cast does exactly this on IEEE
  * hosts (FLT_EVAL_METHOD 0); used only for already-representable values
  * and for the f32 accumulator, whose adds are IEEE binary32 adds. */
@@ -188,6 +218,7 @@ static double load_value(const void* p, size_t i, int t) {
     case ORC_F16: { uint16_t u; memcpy(&u, b, 2); return f16_value(u); }
     case ORC_BF16: { uint16_t u; memcpy(&u, b, 2); return bf16_value(u); }
     case ORC_FP8: return fp8_value(b[0]);
+    case ORC_FP8FN: return fp8fn_value(b[0]);
   }
   return NAN;
 }
@@ -206,6 +237,7 @@ static void store_value(void* p, size_t i, int t, double v) {
     case ORC_F16: { uint16_t u = narrow_f16(v); memcpy(b, &u, 2); break; }
     case ORC_BF16: { uint16_t u = narrow_bf16(v); memcpy(b, &u, 2); break; }
     case ORC_FP8: b[0] = narrow_fp8(v); break;
+    case ORC_FP8FN: b[0] = narrow_fp8fn(v); break;
   }
 }
 
@@ -215,6 +247,7 @@ static double round_to(int t, double v) {
     case ORC_F16: return f16_value(narrow_f16(v));
     case ORC_BF16: return bf16_value(narrow_bf16(v));
     case ORC_FP8: return fp8_value(narrow_fp8(v));
+    case ORC_FP8FN: return fp8fn_value(narrow_fp8fn(v));
     case ORC_F32: return isnan(v) ? v : (double)(float)v;
   }
   return NAN;

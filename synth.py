@@ -13,8 +13,8 @@ from __future__ import annotations
 import torch
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-                "fp8": torch.uint8}
-ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+                "fp8": torch.uint8, "fp8fn": torch.uint8}
+ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -43,11 +43,20 @@ def fp8_finite_codes(count: int, seed: int, device="cpu") -> torch.Tensor:
     return codes.to(torch.uint8)
 
 
+def fp8fn_finite_codes(count: int, seed: int, device="cpu") -> torch.Tensor:
+    """Uniform over the 254 finite OCP FP8 E4M3FN codes (all but 0x7F, 0xFF)."""
+    j = torch.randint(0, 254, (count,), generator=_gen(seed, device), device=device,
+                      dtype=torch.int32)
+    codes = torch.where(j < 127, j, j - 127 + 0x80)
+    return codes.to(torch.uint8)
+
+
 def rank_inputs(kind: str, t: str, nranks: int, count: int, seed0: int = 0,
                 device="cpu") -> list[torch.Tensor]:
     """One buffer per simulated rank; rank r uses seed seed0 + r.
 
-    kind: "normal" (~N(0,1)), "uniform" (~U(-1,1)) or "fp8codes".
+    kind: "normal" (~N(0,1)), "uniform" (~U(-1,1)) or "fp8codes" (uniform over
+    the finite codes of t = "fp8" (E4M3B15) or "fp8fn" (OCP E4M3FN)).
     """
     out = []
     for r in range(nranks):
@@ -56,8 +65,9 @@ def rank_inputs(kind: str, t: str, nranks: int, count: int, seed0: int = 0,
         elif kind == "uniform":
             out.append(uniform(t, count, seed0 + r, device=device))
         elif kind == "fp8codes":
-            assert t == "fp8"
-            out.append(fp8_finite_codes(count, seed0 + r, device))
+            assert t in ("fp8", "fp8fn")
+            gen = fp8_finite_codes if t == "fp8" else fp8fn_finite_codes
+            out.append(gen(count, seed0 + r, device))
         else:
             raise ValueError(kind)
     return out

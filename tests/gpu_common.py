@@ -8,8 +8,9 @@ import torch
 
 import synth
 
-TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8}
-SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8,
+         "fp8fn": torch.uint8}
+SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
 
 
 def announce(*what):
@@ -29,6 +30,8 @@ def is_nan_bits(a: np.ndarray, t: str) -> np.ndarray:
         return (a.view(np.uint16) & 0x7FFF) > 0x7C00
     if t == "bf16":
         return (a.view(np.uint16) & 0x7FFF) > 0x7F80
+    if t == "fp8fn":
+        return (a.view(np.uint8) & 0x7F) == 0x7F
     return (a.view(np.uint8) & 0x7F) > 0x78
 
 
@@ -37,7 +40,8 @@ def assert_bits_equal(got: np.ndarray, want: np.ndarray, t: str, what: str = "")
     g = np.ascontiguousarray(got)
     w = np.ascontiguousarray(want)
     assert g.shape == w.shape, (what, g.shape, w.shape)
-    view = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}[t]
+    view = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8,
+            "fp8fn": np.uint8}[t]
     gn, wn = is_nan_bits(g, t), is_nan_bits(w, t)
     assert np.array_equal(gn, wn), "%s: NaN positions differ" % what
     bad = np.nonzero((g.view(view) != w.view(view)) & ~wn)[0]
@@ -53,7 +57,7 @@ def empty(t: str, count: int, fill=None) -> torch.Tensor:
 
 
 def inputs_for(t: str, n: int, count: int, seed0: int, kind=None, device="cuda"):
-    kind = kind or ("fp8codes" if t == "fp8" else "normal")
+    kind = kind or ("fp8codes" if t in ("fp8", "fp8fn") else "normal")
     return [x.to(device) for x in synth.rank_inputs(kind, t, n, count, seed0, device="cpu")] \
         if device == "cuda" and count * n <= (1 << 24) else \
         synth.rank_inputs(kind, t, n, count, seed0, device=device)

@@ -83,7 +83,9 @@ def test_rsag_argument_checks(lib):
 
 @pytest.mark.parametrize("t,acc,out", [("bf16", "f16", "bf16"), ("f16", "bf16", "f16"),
                                        ("f32", "f16", "f32"), ("f16", "f32", "f32"),
-                                       ("bf16", "f32", "f16"), ("f32", "f32", "fp8")])
+                                       ("bf16", "f32", "f16"), ("f32", "f32", "fp8"),
+                                       ("fp8", "f32", "fp8fn"), ("fp8fn", "fp8", "fp8"),
+                                       ("fp8fn", "f32", "fp8"), ("fp8fn", "bf16", "fp8fn")])
 def test_rsag_unsupported_types(lib, t, acc, out):
     assert rsag(8, t=t, acc=acc, out=out) == mrr.MRR_EUNSUPPORTED
 

@@ -50,6 +50,9 @@ MUTANTS = [
      "uint32_t byte = at < nbytes ? src[at] : 0xFF;"),
     ("scratch indexed [src][dst]", "((size_t)d * nranks + s) * npkt;",
      "((size_t)s * nranks + d) * npkt;"),
+    ("e4m3fn bias 8", "else v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+     "else v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("e4m3fn NaN code finite", "if (e == 0xF && m == 7) v = NAN;", "if (e == 0xF && m == 8) v = NAN;"),
     ("two-phase scratch indexed [src][dst]", "rs[((size_t)c * nranks + d) * cw + k] =",
      "rs[((size_t)d * nranks + c) * cw + k] ="),
     ("two-phase all-gather of the input", "make_packet(word_at((const uint8_t*)outputs[0], nbytes, w), flag);",
@@ -80,6 +83,8 @@ def _checks():
         pins.test_pack_unpack_roundtrip,
         lambda o: pins.test_allreduce_packet_expectation(o, "f16", 1001),
         lambda o: pins.test_packet_rsag_expectation(o, "f16", 1001, 4),
+        pins.test_fp8fn_decode_vs_torch,
+        pins.test_fp8fn_encode_all_f16_brute_force_and_torch,
     ]
 
 

@@ -549,3 +549,82 @@ def test_packet_rsag_expectation(orc, t, count, nranks):
             red = out.view(np.uint8)[lo:lo + chunk_bytes]
             want = orc.pack(red, 5) if red.size else np.zeros(0, np.uint64)
             assert np.array_equal(ag[d, c, :want.size], want)
+
+
+# ---------------------------------------------------------------------------
+# OCP FP8 E4M3FN
+# ---------------------------------------------------------------------------
+
+def torch_fn_values():
+    c = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+FN_VALUES = torch_fn_values()
+FN_MAGS = FN_VALUES[:0x7F]
+
+
+def brute_fn_encode(x):
+    """Nearest finite E4M3FN magnitude (exhaustive), ties to the even code,
+    saturating at 448; NaN -> 0x7F|s.  float64 distances are exact wherever
+    the choice depends on them (|x| <= 512, ulp >= 2^-41 near midpoints)."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    a = np.abs(x)
+    a_fin = np.where(np.isfinite(a), np.minimum(a, 512.0), 512.0)
+    d = np.abs(a_fin[:, None] - FN_MAGS[None, :])
+    i = np.argmin(d, axis=1)
+    nxt = np.minimum(i + 1, 0x7E)
+    tie = (nxt != i) & (d[np.arange(len(i)), nxt] == d[np.arange(len(i)), i])
+    i = np.where(tie & (i % 2 == 1), nxt, i)
+    sign = np.where(np.signbit(x), 0x80, 0)
+    return np.where(np.isnan(x), sign | 0x7F, i | sign).astype(np.uint8)
+
+
+def test_fp8fn_decode_vs_torch(orc):
+    v = orc.widen_f64(np.arange(256, dtype=np.uint8), "fp8fn")
+    assert same_bits_or_both_nan(v, FN_VALUES)
+    assert np.nanmax(v) == 448.0 and v[1] == 2.0 ** -9 and np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.isfinite(v).sum() == 254
+
+
+def test_fp8fn_encode_all_f16_brute_force_and_torch(orc):
+    h = np.arange(65536, dtype=np.uint16)
+    x = np_f16(h).astype(np.float64)
+    got = orc.convert(h, "f16", "fp8fn")
+    assert_codes_equal(got, brute_fn_encode(x))
+    # torch's own cast agrees wherever it does not overflow (it gives NaN there)
+    ok = np.abs(x) < 464
+    want = torch.from_numpy(x[ok].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert_codes_equal(got[ok], want)
+    assert list(orc.narrow_f64(np.array([464.0, 480.0, 1e9, np.inf, -np.inf, -500.0]), "fp8fn")) == \
+        [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+
+
+@pytest.mark.parametrize("nranks", [2, 8, 32])
+def test_fp8fn_f32_accumulation_is_exact(orc, nranks):
+    """E4M3FN values are k * 2^-9 with |k| <= 229376, so <= 32 of them sum
+    exactly in f32; every output is the exact sum rounded once."""
+    import synth
+    n = 50000
+    xs = [synth.fp8fn_finite_codes(n, 1300 + r).numpy() for r in range(nranks)]
+    k = sum(np.rint(FN_VALUES[x] * 2.0 ** 9).astype(np.int64) for x in xs)
+    exact = k.astype(np.float64) * 2.0 ** -9
+    exact = np.where(np.logical_and.reduce([x == 0x80 for x in xs]), -0.0, exact)
+    got32 = orc.allreduce(xs, "fp8fn", "f32", "f32")
+    assert np.array_equal(got32.view(np.uint32), exact.astype(np.float32).view(np.uint32))
+    assert_codes_equal(orc.allreduce(xs, "fp8fn", "f32", "f16"), exact.astype(np.float16).view(np.uint16))
+    assert_codes_equal(orc.allreduce(xs, "fp8fn", "f32", "fp8fn"), brute_fn_encode(exact))
+
+
+def test_fp8fn_native_accumulation_and_accuracy(orc):
+    import synth
+    n, nranks = 20000, 8
+    xs = [synth.fp8fn_finite_codes(n, 1400 + r).numpy() for r in range(nranks)]
+    acc = brute_fn_encode(FN_VALUES[xs[0]])
+    for x in xs[1:]:
+        acc = brute_fn_encode(FN_VALUES[acc] + FN_VALUES[x])
+    assert_codes_equal(orc.allreduce(xs, "fp8fn", "fp8fn", "fp8fn"), acc)
+    exact = sum(FN_VALUES[x] for x in xs)
+    e32 = np.abs(orc.widen_f64(orc.allreduce(xs, "fp8fn", "f32", "fp8fn"), "fp8fn") - exact)
+    e8 = np.abs(FN_VALUES[acc] - exact)
+    assert np.all(e32 <= e8)
