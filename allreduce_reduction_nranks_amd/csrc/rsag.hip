@@ -45,14 +45,15 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup
 //   FP8 inputs (E4M3B15 and OCP E4M3FN): U=4 for N=2, else 1, times 2 for
 //                             f16 and 4 for f32 outputs
 //                             (so a lane still loads 16 bytes per rank);
-//                             workgroups per CU: 4 (FP8 out), 3 (f16 out),
-//                             4 (f32 out).
+//                             workgroups per CU: 4 (E4M3B15 out), 6 (E4M3FN
+//                             out, whose shorter body needs more waves in
+//                             flight), 3 (f16 out), 4 (f32 out).
 constexpr int rsag_unroll(int n, int tin, int tout) {
   if (is_fp8(tin)) return (n == 2 ? 4 : 1) * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
   return n == 2 ? 8 : n == 4 ? 4 : n == 16 ? 2 : 1;
 }
 constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
-  if (is_fp8(tin)) return tout == kF16 ? 3 : 4;
+  if (is_fp8(tin)) return tout == kF16 ? 3 : tout == kFP8FN ? 6 : 4;
   return n == 2 ? 2 : n == 4 ? 4 : n == 8 ? 6 : n == 16 ? 2 : 8;
 }
 // Ranks whose vectors are loaded together before they are added: all of them
