@@ -5,9 +5,14 @@
 // 0.9375, converted through fp16 as intermediate); ROCm support entry.
 // Decoding is exact; encoding is one round-to-nearest-even, saturating.
 //
-// Elementwise and HBM-bound.  A lane handles a unit of 16 elements: 16 bytes
-// of FP8, 32 bytes of f16 or 64 bytes of f32, all moved with non-temporal
-// 16-byte accesses; the last n % 16 elements go element by element.
+// Elementwise and HBM-bound.  A lane converts units of V elements, where the
+// wider side of a unit is one 16-byte vector and the narrower side 4 or 8
+// bytes; consecutive lanes take consecutive units, so every load and every
+// store instruction of a wave covers one contiguous span (1 KiB on the wide
+// side, 256 or 512 B on the narrow side) and writes whole cache lines.  Each
+// lane keeps U units in flight; the last n % V elements go one by one.
+#include <cstdlib>
+
 #include "mrr_device.hpp"
 #include "mrr_internal.hpp"
 
@@ -15,52 +20,47 @@ namespace mrr {
 
 enum : int { kDecF16 = 0, kDecF32 = 1, kEncF16 = 2, kEncF32 = 3 };
 
-template <int Dir> __device__ __forceinline__ void codec_unit(const void* in, void* out, uint64_t u) {
-  if constexpr (Dir == kDecF16 || Dir == kDecF32) {
-    const u32x4 c = ld_stream(in, u);
-    if constexpr (Dir == kDecF16) {
-      u32x4 o[2];
+// V elements per unit; DI input words and DO output words per unit.
+template <int Dir> struct CodecShape;
+template <> struct CodecShape<kDecF16> { static constexpr int V = 8, DI = 2, DO = 4; };
+template <> struct CodecShape<kDecF32> { static constexpr int V = 4, DI = 1, DO = 4; };
+template <> struct CodecShape<kEncF16> { static constexpr int V = 8, DI = 4, DO = 2; };
+template <> struct CodecShape<kEncF32> { static constexpr int V = 4, DI = 4, DO = 1; };
+
+// Stores D words as unit `unit` of a buffer, non-temporal.
+template <int D> __device__ __forceinline__ void st_words(void* base, uint64_t unit, const uint32_t* w) {
+  typedef typename WordsT<D>::type Vt;
+  Vt v;
+  if constexpr (D == 1) {
+    v = w[0];
+  } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = c[j];
-        const uint32_t lo = fp8_to_f16(w & 0xFFu) | (fp8_to_f16((w >> 8) & 0xFFu) << 16);
-        const uint32_t hi = fp8_to_f16((w >> 16) & 0xFFu) | (fp8_to_f16(w >> 24) << 16);
-        o[j / 2][(j % 2) * 2] = lo;
-        o[j / 2][(j % 2) * 2 + 1] = hi;
-      }
-      st_stream(out, 2 * u, o[0]);
-      st_stream(out, 2 * u + 1, o[1]);
-    } else {
+    for (int j = 0; j < D; ++j) v[j] = w[j];
+  }
+  __builtin_nontemporal_store(v, reinterpret_cast<Vt*>(base) + unit);
+}
+
+template <int Dir> __device__ __forceinline__ void convert_unit(const uint32_t* in, uint32_t* out) {
+  if constexpr (Dir == kDecF16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 o;
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t w = in[j];
+      out[2 * j] = fp8_to_f16(w & 0xFFu) | (fp8_to_f16((w >> 8) & 0xFFu) << 16);
+      out[2 * j + 1] = fp8_to_f16((w >> 16) & 0xFFu) | (fp8_to_f16(w >> 24) << 16);
+    }
+  } else if constexpr (Dir == kDecF32) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) o[b] = __float_as_uint(fp8_to_f32((c[j] >> (8 * b)) & 0xFFu));
-        st_stream(out, 4 * u + j, o);
-      }
+    for (int b = 0; b < 4; ++b) out[b] = __float_as_uint(fp8_to_f32((in[0] >> (8 * b)) & 0xFFu));
+  } else if constexpr (Dir == kEncF16) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t w0 = in[2 * j], w1 = in[2 * j + 1];
+      out[j] = f16_to_fp8(w0 & 0xFFFFu) | (f16_to_fp8(w0 >> 16) << 8) |
+               (f16_to_fp8(w1 & 0xFFFFu) << 16) | (f16_to_fp8(w1 >> 16) << 24);
     }
   } else {
-    u32x4 o;
-    if constexpr (Dir == kEncF16) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const u32x4 h = ld_stream(in, 2 * u + q);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t w0 = h[2 * j], w1 = h[2 * j + 1];
-          o[2 * q + j] = f16_to_fp8(w0 & 0xFFFFu) | (f16_to_fp8(w0 >> 16) << 8) |
-                         (f16_to_fp8(w1 & 0xFFFFu) << 16) | (f16_to_fp8(w1 >> 16) << 24);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 f = ld_stream(in, 4 * u + q);
-        o[q] = f32_to_fp8(__uint_as_float(f[0])) | (f32_to_fp8(__uint_as_float(f[1])) << 8) |
-               (f32_to_fp8(__uint_as_float(f[2])) << 16) | (f32_to_fp8(__uint_as_float(f[3])) << 24);
-      }
-    }
-    st_stream(out, u, o);
+    out[0] = f32_to_fp8(__uint_as_float(in[0])) | (f32_to_fp8(__uint_as_float(in[1])) << 8) |
+             (f32_to_fp8(__uint_as_float(in[2])) << 16) | (f32_to_fp8(__uint_as_float(in[3])) << 24);
   }
 }
 
@@ -75,42 +75,102 @@ template <int Dir> __device__ __forceinline__ void codec_elem(const void* in, vo
     reinterpret_cast<uint8_t*>(out)[i] = (uint8_t)f32_to_fp8(reinterpret_cast<const float*>(in)[i]);
 }
 
-// Vector path: units [0, n / 16) then the tail, both grid-stride.
-template <int Dir>
-__global__ void __launch_bounds__(256) codec_vec_k(const void* in, void* out, uint64_t n) {
-  const uint64_t units = n / 16;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (uint64_t u = tid; u < units; u += stride) codec_unit<Dir>(in, out, u);
-  for (uint64_t i = units * 16 + tid; i < n; i += stride) codec_elem<Dir>(in, out, i);
+constexpr int kCodecThreads = 256;
+
+// Vector path: tiles of kCodecThreads * U units, grid-stride, then the tail.
+template <int Dir, int U>
+__global__ void __launch_bounds__(kCodecThreads) codec_vec_k(const void* in, void* out, uint64_t n) {
+  using S = CodecShape<Dir>;
+  const uint64_t units = n / S::V;
+  const uint64_t tile = (uint64_t)kCodecThreads * U;
+  for (uint64_t t0 = (uint64_t)blockIdx.x * tile; t0 < units; t0 += (uint64_t)gridDim.x * tile) {
+    const uint64_t v0 = t0 + threadIdx.x;
+    if (t0 + tile <= units) {
+      uint32_t w[U][S::DI];
+#pragma unroll
+      for (int u = 0; u < U; ++u) ld_words<S::DI>(in, v0 + (uint64_t)u * kCodecThreads, w[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint32_t o[S::DO];
+        convert_unit<Dir>(w[u], o);
+        st_words<S::DO>(out, v0 + (uint64_t)u * kCodecThreads, o);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t v = v0 + (uint64_t)u * kCodecThreads;
+        if (v < units) {
+          uint32_t w[S::DI], o[S::DO];
+          ld_words<S::DI>(in, v, w);
+          convert_unit<Dir>(w, o);
+          st_words<S::DO>(out, v, o);
+        }
+      }
+    }
+  }
+  const uint64_t stride = (uint64_t)gridDim.x * kCodecThreads;
+  for (uint64_t i = units * S::V + (uint64_t)blockIdx.x * kCodecThreads + threadIdx.x; i < n; i += stride)
+    codec_elem<Dir>(in, out, i);
 }
 
 template <int Dir>
-__global__ void __launch_bounds__(256) codec_scalar_k(const void* in, void* out, uint64_t n) {
+__global__ void __launch_bounds__(kCodecThreads) codec_scalar_k(const void* in, void* out, uint64_t n) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
     codec_elem<Dir>(in, out, i);
 }
 
-hipError_t launch_codec(int dir, const void* in, void* out, size_t n, bool vector,
-                        hipStream_t stream) {
-  const uint64_t work = vector ? (n / 16 > 0 ? n / 16 : 1) : n;
-  uint64_t blocks = (work + 255) / 256;
-  const uint64_t cap = (uint64_t)device_cu_count(-1) * 16;
+// Units in flight per lane and 256-lane workgroups per CU, per direction,
+// measured on MI355X over 268,435,456 elements (U in {1,2,4,8} x {4,8,16}
+// workgroups per CU): U=8 and 16 per CU for both decodes and the f16 encode;
+// the f32 encode, whose lanes already load 64 B per unit group, is best at
+// U=4 and 4 per CU.  MRR_CODEC_U / MRR_CODEC_WPC override.
+constexpr int codec_unroll(int dir) { return dir == kEncF32 ? 4 : 8; }
+constexpr int codec_wg_per_cu(int dir) { return dir == kEncF32 ? 4 : 16; }
+
+template <int Dir, int U>
+static void launch_vec_u(dim3 grid, const void* in, void* out, uint64_t n, hipStream_t s) {
+  hipLaunchKernelGGL((codec_vec_k<Dir, U>), grid, dim3(kCodecThreads), 0, s, in, out, n);
+}
+
+template <int Dir>
+static hipError_t launch_codec_dir(const void* in, void* out, uint64_t n, bool vector,
+                                   hipStream_t stream) {
+  static const int u_env = [] { const char* v = getenv("MRR_CODEC_U"); return v ? atoi(v) : 0; }();
+  static const int wpc_env = [] { const char* v = getenv("MRR_CODEC_WPC"); return v ? atoi(v) : 0; }();
+  const int U = (u_env == 1 || u_env == 2 || u_env == 4 || u_env == 8) ? u_env : codec_unroll(Dir);
+  const uint64_t wpc = wpc_env > 0 ? (uint64_t)wpc_env : (uint64_t)codec_wg_per_cu(Dir);
+  const uint64_t units = n / CodecShape<Dir>::V;
+  const uint64_t work = vector ? (units + (uint64_t)kCodecThreads * U - 1) / ((uint64_t)kCodecThreads * U)
+                               : (n + kCodecThreads - 1) / kCodecThreads;
+  uint64_t blocks = work;
+  uint64_t cap = (uint64_t)device_cu_count(-1) * wpc;
+  if (cap == 0) cap = 2048;
   if (blocks > cap) blocks = cap;
-  if (blocks == 0) blocks = 1;
-  const dim3 grid((uint32_t)blocks), block(256);
-  switch (dir) {
-#define MRR_DIR(D)                                                                          \
-  case D:                                                                                   \
-    if (vector) hipLaunchKernelGGL(codec_vec_k<D>, grid, block, 0, stream, in, out, (uint64_t)n); \
-    else hipLaunchKernelGGL(codec_scalar_k<D>, grid, block, 0, stream, in, out, (uint64_t)n); \
-    break;
-    MRR_DIR(kDecF16) MRR_DIR(kDecF32) MRR_DIR(kEncF16) MRR_DIR(kEncF32)
-#undef MRR_DIR
-    default: return hipErrorInvalidValue;
+  if (blocks == 0) blocks = 1;  // tail only
+  const dim3 grid((uint32_t)blocks);
+  if (!vector) {
+    hipLaunchKernelGGL(codec_scalar_k<Dir>, grid, dim3(kCodecThreads), 0, stream, in, out, n);
+  } else {
+    switch (U) {
+      case 1: launch_vec_u<Dir, 1>(grid, in, out, n, stream); break;
+      case 2: launch_vec_u<Dir, 2>(grid, in, out, n, stream); break;
+      case 4: launch_vec_u<Dir, 4>(grid, in, out, n, stream); break;
+      default: launch_vec_u<Dir, 8>(grid, in, out, n, stream); break;
+    }
   }
   return hipGetLastError();
+}
+
+hipError_t launch_codec(int dir, const void* in, void* out, size_t n, bool vector,
+                        hipStream_t stream) {
+  switch (dir) {
+    case kDecF16: return launch_codec_dir<kDecF16>(in, out, n, vector, stream);
+    case kDecF32: return launch_codec_dir<kDecF32>(in, out, n, vector, stream);
+    case kEncF16: return launch_codec_dir<kEncF16>(in, out, n, vector, stream);
+    case kEncF32: return launch_codec_dir<kEncF32>(in, out, n, vector, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace mrr

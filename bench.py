@@ -14,9 +14,11 @@ measured with HIP events on the launch stream.  ``cpu_baseline`` times the
 CPU oracle on a bounded sample of the same workload.
 
 Other configurations (--config): c1 (2 x 1 MiB bf16), c3 (LL-packet allpair,
-8 ranks, --size KiB), c4 (8 x 32 MiB FP8 E4M3B15 -> f16 or fp8 via --out),
+8 ranks, --size KiB), c4 (8 x 32 MiB FP8 -> f16, f32 or FP8 via --out; --fp8 picks
+E4M3B15 or OCP E4M3FN),
 c5 (N x 256 MiB bf16 via --nranks), custom (--nranks N --size KiB --dtype T; rank
-counts outside 2/4/8/16/32 run the runtime-N kernel through mrr_allreduce).
+counts outside 2/4/8/16/32 run the runtime-N kernel through mrr_allreduce),
+codec (the standalone E4M3B15 codec over 8 x 32 MiB codes, --dir).
 """
 from __future__ import annotations
 
@@ -38,21 +40,24 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["allreduce_reduction_nranks_amd/csrc/rsag.hip",
                   "allreduce_reduction_nranks_amd/csrc/mrr_device.hpp",
                   "allreduce_reduction_nranks_amd/csrc/mrr_internal.hpp"]
+CODEC_SOURCES = ["allreduce_reduction_nranks_amd/csrc/codec.hip",
+                 "allreduce_reduction_nranks_amd/csrc/mrr_device.hpp",
+                 "allreduce_reduction_nranks_amd/csrc/mrr_internal.hpp"]
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_key: str):
+def measured_traffic(workload_key: str, sources=None):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
     None when it is missing or was taken on different kernel sources."""
     path = os.path.join(PROFILE_DIR, "%s_pmc.txt" % workload_key)
@@ -63,7 +68,7 @@ def measured_traffic(workload_key: str):
         parts = line.split()
         if len(parts) >= 2 and not line.startswith("#"):
             vals[parts[0]] = parts[1]
-    if vals.get("kernel_source_hash") != kernel_source_hash():
+    if vals.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -267,12 +272,78 @@ def bench_packet(args, torch, mrr, synth):
     }
 
 
+CODEC = {  # --dir: (entry point, input type, output type)
+    "dec16": ("mrr_fp8b15_to_f16", "fp8", "f16"), "dec32": ("mrr_fp8b15_to_f32", "fp8", "f32"),
+    "enc16": ("mrr_f16_to_fp8b15", "f16", "fp8"), "enc32": ("mrr_f32_to_fp8b15", "f32", "fp8")}
+
+
+def bench_codec(args, torch, mrr, synth):
+    """Standalone FP8 E4M3B15 codec over the FP8 workload's volume: 8 x 32 MiB
+    codes as one buffer of 268,435,456 elements, one launch per step."""
+    fn_name, tin, tout = CODEC[args.dir]
+    n = 8 * 32 * MiB
+    if tin == "fp8":
+        src = synth.fp8_finite_codes(n, args.seed0, device="cuda")
+        kind = "uniform over the 240 finite E4M3B15 codes"
+    else:
+        src = synth.uniform(tin, n, args.seed0, device="cuda")
+        kind = "%s ~U(-1,1)" % tin
+    dst = torch.empty(n * ESIZE[tout], dtype=torch.uint8, device="cuda")
+    fn = getattr(mrr, fn_name)
+    torch.cuda.synchronize()
+
+    def step():
+        st = fn(src, dst, n)
+        if st != mrr.MRR_OK:
+            raise mrr.MrrError(st)
+
+    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    alg_bytes = n * (ESIZE[tin] + ESIZE[tout])
+    value = alg_bytes / (wall_ms * 1e-3) / 1e9
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    key = "codec_%s_256Mi" % args.dir
+    ceiling = copy_ceiling(torch, n * ESIZE[tin]) if args.copy_ceiling else None
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8" if tin == "fp8" and tout == "f16" else "f32",
+        "data": "synthetic (seeded %d), %s" % (args.seed0, kind),
+        "config": {"workload": "FP8 E4M3B15 codec %s, %s -> %s, 268,435,456 elements (8 x 32 MiB "
+                               "codes)" % (fn_name, tin, tout),
+                   "count": n, "in": tin, "out": tout, "algorithmic_bytes_per_call": alg_bytes,
+                   "kernel_us": round(kern_ms * 1e3, 2),
+                   "pct_of_hbm_peak": round(100 * value / PEAK_GBPS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": measured_traffic(key, CODEC_SOURCES)},
+    }
+    if ceiling is not None:
+        result["config"]["copy_ceiling_gbps"] = round(ceiling, 2)
+    if args.cpu_baseline:
+        import oracle
+        sample = min(n, args.cpu_sample)
+        host = synth.to_bits_numpy(src[:sample])
+        oracle.default()
+        t0 = time.perf_counter()
+        oracle.convert(host, tin, tout)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(sample * (ESIZE[tin] + ESIZE[tout]) / dt / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "first %d elements (%.1f%% of the workload), one thread, %.1f s"
+                      % (sample, 100.0 * sample / n, dt)}
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "custom"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "custom", "codec"])
+    ap.add_argument("--dir", default="dec16", choices=sorted(CODEC),
+                    help="codec: direction (dec16/dec32 = E4M3B15 -> f16/f32, enc16/enc32 = back)")
     ap.add_argument("--dtype", default="f16", choices=["f32", "f16", "bf16", "fp8", "fp8fn"],
                     help="custom: type (fp8 = E4M3B15, fp8fn = OCP E4M3FN)")
     ap.add_argument("--nranks", type=int, default=8, help="c5: rank count")
@@ -310,6 +381,8 @@ def main():
     mrr.load_library()
     if args.config == "c3":
         result = bench_packet(args, torch, mrr, synth)
+    elif args.config == "codec":
+        result = bench_codec(args, torch, mrr, synth)
     else:
         result = bench_rsag(args, torch, mrr, synth)
     print(json.dumps(result), flush=True)
