@@ -305,11 +305,35 @@ static void launch_vec_typed(int nranks, dim3 grid, const RsagArgs& a, hipStream
 }
 
 // The runtime-N kernel loads 16 bytes per lane per rank like the compiled
-// ones at N = 8; one unit per lane, 6 workgroups per CU.
+// ones at N = 8, times a multiplier M of units per lane for 16- and 32-bit
+// inputs so that small rank counts still keep enough loads in flight.
+// Measured on MI355X (64-128 MiB per rank; M in {1,2,4} x 2-8 workgroups per
+// CU): N <= 4: M=4, 8 per CU; N <= 8: M=2, 4 per CU; N <= 16: M=1, 4 per CU;
+// N > 16: M=1, 2 per CU.  FP8 inputs keep M=1 and 6 per CU.
+// MRR_RSAG_ANY_M and MRR_RSAG_WPC override.
 constexpr int rsag_any_unroll(int tin, int tout) {
   return is_fp8(tin) ? (tout == kF32 ? 4 : tout == kF16 ? 2 : 1) : 1;
 }
-constexpr int kAnyWgPerCu = 6;
+static int rsag_any_multiplier(int n) { return n <= 4 ? 4 : n <= 8 ? 2 : 1; }
+static int rsag_any_wg_per_cu(int n, int tin) {
+  if (is_fp8(tin)) return 6;
+  return n <= 4 ? 8 : n <= 16 ? 4 : 2;
+}
+
+template <int In, int Acc, int Out>
+static void launch_any_typed(int mult, dim3 grid, const RsagArgs& a, hipStream_t s) {
+  constexpr int U = rsag_any_unroll(In, Out);
+  if constexpr (is_fp8(In)) {
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U>), grid, dim3(kRsagThreads), 0, s, a);
+  } else {
+    if (mult == 4)
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 4 * U>), grid, dim3(kRsagThreads), 0, s, a);
+    else if (mult == 2)
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 2 * U>), grid, dim3(kRsagThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U>), grid, dim3(kRsagThreads), 0, s, a);
+  }
+}
 
 // Plans and launches one type triple.  The chunk and unit geometry comes from
 // the same compile-time element sizes the kernels index with (Ty, Unit), so
@@ -338,10 +362,36 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     a.tail_begin = a.total_vecs * ue;
     const uint32_t tail = (uint32_t)(count - a.tail_begin);
     const uint64_t tail_chunk = a.chunk_vecs ? a.total_vecs / a.chunk_vecs : 0;
-    const bool any_n = !valid_nranks(n);
+    // Small calls: when the table's U would leave fewer than 2 tiles per CU,
+    // CUs sit idle; the runtime-N kernel at one unit group per lane spreads
+    // the same work over U times more workgroups (measured under HIP-graph
+    // replay: 2 x 1 MiB bf16 2.44 -> 2.27 us, 4 x 256 KiB f16 2.39 -> 2.19 us).
+    // Only while its ranks fit one load group (N <= 8): at N = 16 the split
+    // into two dependent groups costs more than it gains (3.14 -> 3.44 us).
+    // MRR_RSAG_SMALL=0 disables.
+    static const bool small_ok = [] {
+      const char* v = getenv("MRR_RSAG_SMALL");
+      return !(v && v[0] == '0');
+    }();
+    bool small = false;
+    if (valid_nranks(n) && n <= kAnyGroup && small_ok &&
+        rsag_unroll(n, In, Out) > rsag_any_unroll(In, Out)) {
+      const uint64_t vec_tile = (uint64_t)kRsagThreads * rsag_unroll(n, In, Out);
+      const uint64_t vec_tiles = (uint64_t)(p.rank < 0 ? n : 1) * ((a.chunk_vecs + vec_tile - 1) / vec_tile);
+      small = vec_tiles < 2 * (uint64_t)(device_cu_count(-1) > 0 ? device_cu_count(-1) : 256);
+    }
+    const bool any_n = !valid_nranks(n) || small;
     a.nranks = (uint32_t)n;
+    int mult = 1;
+    if (any_n && !small && !is_fp8(In)) {
+      static const int m_env = [] {
+        const char* v = getenv("MRR_RSAG_ANY_M");
+        return v ? atoi(v) : 0;
+      }();
+      mult = (m_env == 1 || m_env == 2 || m_env == 4) ? m_env : rsag_any_multiplier(n);
+    }
     const uint64_t tile_vecs =
-        (uint64_t)kRsagThreads * (any_n ? rsag_any_unroll(In, Out) : rsag_unroll(n, In, Out));
+        (uint64_t)kRsagThreads * (any_n ? rsag_any_unroll(In, Out) * mult : rsag_unroll(n, In, Out));
     a.tiles_per_chunk = (uint32_t)((a.chunk_vecs + tile_vecs - 1) / tile_vecs);
     uint32_t nchunks;
     if (p.rank < 0) {
@@ -356,7 +406,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     a.launch_tiles = nchunks * a.tiles_per_chunk;
     if (a.launch_tiles == 0 && a.tail_count == 0) return hipSuccess;
     // Persistent grid: wg_per_cu workgroups per CU (MRR_RSAG_WPC overrides).
-    int wpc = any_n ? kAnyWgPerCu : rsag_wg_per_cu(n, In, Out);
+    int wpc = small ? 8 : any_n ? rsag_any_wg_per_cu(n, In) : rsag_wg_per_cu(n, In, Out);
     static const int wpc_env = [] {
       const char* v = getenv("MRR_RSAG_WPC");
       return v ? atoi(v) : 0;
@@ -368,8 +418,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     if (blocks == 0) blocks = 1;  // tail only
     const dim3 grid((uint32_t)blocks);
     if (any_n)
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, rsag_any_unroll(In, Out)>), grid,
-                         dim3(kRsagThreads), 0, stream, a);
+      launch_any_typed<In, Acc, Out>(mult, grid, a, stream);
     else
       launch_vec_typed<In, Acc, Out>(n, grid, a, stream);
   } else {

@@ -37,6 +37,8 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 MiB = 1 << 20
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+TIMING_EAGER = "HIP events around K eager calls on the launch stream"
+TIMING_GRAPH = "HIP events around one replay of a HIP graph holding the K calls"
 KERNEL_SOURCES = ["allreduce_reduction_nranks_amd/csrc/rsag.hip",
                   "allreduce_reduction_nranks_amd/csrc/mrr_device.hpp",
                   "allreduce_reduction_nranks_amd/csrc/mrr_internal.hpp"]
@@ -101,6 +103,43 @@ class Timer:
         wall_ms = (t1 - t0) * 1e3 / steps
         kern_ms = e0.elapsed_time(e1) / steps
         return wall_ms, kern_ms
+
+    def run_graph(self, fn, steps, warmup):
+        """The K calls captured once into a HIP graph and replayed: per-call
+        GPU time without the host's per-call launch cost (what a captured
+        inference step sees).  The library's calls allocate nothing and keep
+        their state on the device, so replays are valid calls."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(steps):
+                    fn()
+        torch.cuda.synchronize()
+        g.replay()  # warm replay
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def use_graph(args, alg_bytes):
+    """--graph auto: graph timing for calls that move under 64 MiB, where the
+    host's per-call cost (ctypes + launch, several us) would otherwise be
+    what is measured."""
+    return args.graph == "on" or (args.graph == "auto" and alg_bytes < 64 * MiB)
 
 
 def copy_ceiling(torch, nbytes, steps=10):
@@ -182,7 +221,14 @@ def bench_rsag(args, torch, mrr, synth):
         if st != mrr.MRR_OK:
             raise mrr.MrrError(st)
 
-    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    alg_bytes = n * count * (ESIZE[t] + ESIZE[tout])
+    graph = use_graph(args, alg_bytes)
+    eager_us = None
+    if graph:
+        eager_us = Timer(torch).run(step, args.steps, args.warmup)[1] * 1e3
+        wall_ms, kern_ms = Timer(torch).run_graph(step, args.steps, args.warmup)
+    else:
+        wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
     sep_us = None
     if args.layout == "pitch":
         def step_sep():
@@ -190,8 +236,8 @@ def bench_rsag(args, torch, mrr, synth):
                 if compiled else mrr.mrr_allreduce(ins_sep, outs_sep, count, t, acc, n)
             if st != mrr.MRR_OK:
                 raise mrr.MrrError(st)
-        sep_us = Timer(torch).run(step_sep, args.steps, args.warmup)[1] * 1e3
-    alg_bytes = n * count * (ESIZE[t] + ESIZE[tout])
+        timer = Timer(torch)
+        sep_us = (timer.run_graph if graph else timer.run)(step_sep, args.steps, args.warmup)[1] * 1e3
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     key = {"c1": "rsag_2x1MiB_bf16", "c2": "rsag_8x64MiB_f16",
@@ -226,6 +272,9 @@ def bench_rsag(args, torch, mrr, synth):
         result["config"]["copy_ceiling_gbps"] = round(ceiling, 2)
     if sep_us is not None:
         result["config"]["kernel_us_one_allocation_per_rank"] = round(sep_us, 2)
+    result["config"]["timing"] = TIMING_GRAPH if graph else TIMING_EAGER
+    if eager_us is not None:
+        result["config"]["eager_us_per_call"] = round(eager_us, 2)
     if args.cpu_baseline:
         sample = min(count, args.cpu_sample)
         result["cpu_baseline"] = cpu_baseline_rsag(ins, t, acc, tout, sample)
@@ -251,10 +300,16 @@ def bench_packet(args, torch, mrr, synth):
         if st != mrr.MRR_OK:
             raise mrr.MrrError(st)
 
-    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    S = count * 2
+    graph = use_graph(args, 3 * n * S + 4 * n * (n - 1) * S)
+    eager_us = None
+    if graph:
+        eager_us = Timer(torch).run(step, args.steps, args.warmup)[1] * 1e3
+        wall_ms, kern_ms = Timer(torch).run_graph(step, args.steps, args.warmup)
+    else:
+        wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
     if int(err.item()) != 0:
         raise RuntimeError("packet poll timed out")
-    S = count * 2
     # allpair: send reads NS, packets 2N(N-1)S written and read, own input NS, outputs NS.
     # two-phase: input NS; rs packets 2(N-1)S written and read; own chunk S; outputs NS;
     # ag packets 2(N-1)S written and read.
@@ -268,7 +323,9 @@ def bench_packet(args, torch, mrr, synth):
         "config": {"workload": "%s allreduce, 8 ranks x %d KiB f16" % (name, args.size),
                    "nranks": n, "bytes_per_rank": S, "blocks_per_rank": args.blocks,
                    "threads": args.threads, "algorithmic_bytes_per_call": alg_bytes,
-                   "algorithmic_gbps": round(alg_bytes / (kern_ms * 1e-3) / 1e9, 2)},
+                   "algorithmic_gbps": round(alg_bytes / (kern_ms * 1e-3) / 1e9, 2),
+                   "timing": TIMING_GRAPH if graph else TIMING_EAGER,
+                   "eager_us_per_call": None if eager_us is None else round(eager_us, 3)},
     }
 
 
@@ -364,6 +421,8 @@ def main():
                     help="elements per rank the CPU oracle baseline reduces")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-copy-ceiling", dest="copy_ceiling", action="store_false")
+    ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
+                    help="time a HIP graph of the K calls (auto: when a call moves < 64 MiB)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

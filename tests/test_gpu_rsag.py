@@ -48,6 +48,37 @@ def test_parity_small(n, t, acc, tout):
     check_all(outs, want, tout, "n=%d %s/%s/%s" % (n, t, acc, tout))
 
 
+# Calls whose compiled kernel would have fewer than 2 tiles per CU run the
+# runtime-N kernel instead (N = 2, 4 for 16/32-bit data, N = 2 for FP8), so
+# test_parity_small covers that route for them.  These sizes put the same
+# rank counts well above that threshold (3x, on 256 CUs) so the compiled
+# kernels, at the units per lane of their launch table, are covered too.
+FN_TRIPLES = [("fp8fn", a, o) for a in ("f32", "f16", "fp8fn") for o in ("fp8fn", "f16", "f32")]
+OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
+
+
+def table_unroll(n, t, tout):
+    if t in ("fp8", "fp8fn"):
+        return (4 if n == 2 else 1) * {"f32": 4, "f16": 2}.get(tout, 1)
+    return {2: 8, 4: 4, 16: 2}.get(n, 1)
+
+
+VEC_CASES = [(n, t, a, o) for (t, a, o) in TRIPLES + FN_TRIPLES
+             for n in ((2,) if t in ("fp8", "fp8fn") else (2, 4, 16))]
+
+
+@pytest.mark.parametrize("n,t,acc,tout", VEC_CASES, ids=["%d-%s-%s-%s" % c for c in VEC_CASES])
+def test_parity_compiled_kernel_sizes(n, t, acc, tout):
+    u = table_unroll(n, t, tout)
+    ue = 16 // OUT_SIZE[tout]
+    count = n * 64 * u * (3 * 512 // n + 1) * ue + 13
+    announce("rsag compiled-kernel size", n, t, acc, tout, count)
+    ins = inputs_for(t, n, count, seed0=30 * n + 1)
+    outs = run(ins, t, acc, tout)
+    want = oracle.allreduce([bits(x) for x in ins], t, acc, tout)
+    check_all(outs, want, tout, "n=%d %s/%s/%s" % (n, t, acc, tout))
+
+
 @pytest.mark.parametrize("t", ["f32", "f16", "bf16", "fp8"])
 @pytest.mark.parametrize("count", [1, 3, 7, 8, 9, 15, 16, 17, 31, 33, 127, 129, 4095, 4097])
 def test_edge_counts(t, count):
