@@ -174,11 +174,13 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a
 }
 
 // Runtime rank count (1..32): the fallback for counts without a compiled
-// kernel.  Ranks are taken in groups of 8 behind wavefront-uniform bounds,
-// in rank order, with the same unit structure as reduce_store.
+// kernel.  Ranks are taken in groups of G (8 up to 8 ranks, else 16) behind
+// wavefront-uniform bounds, in rank order, with the same unit structure as
+// reduce_store: all loads of a group are issued before its first add.
 constexpr int kAnyGroup = 8;
+constexpr int kAnyGroupWide = 16;
 
-template <int In, int Acc, int Out, int UU>
+template <int In, int Acc, int Out, int UU, int G>
 __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint64_t v0) {
   constexpr int UE = Unit<In, Out>::UE;
   constexpr int D = Unit<In, Out>::D;
@@ -187,18 +189,18 @@ __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint6
   bool special[UU];
 #pragma unroll
   for (int u = 0; u < UU; ++u) special[u] = false;
-  for (int g = 0; g < n; g += kAnyGroup) {
-    uint32_t raw[UU][kAnyGroup][D];
+  for (int g = 0; g < n; g += G) {
+    uint32_t raw[UU][G][D];
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
 #pragma unroll
-      for (int r = 0; r < kAnyGroup; ++r)
+      for (int r = 0; r < G; ++r)
         if (g + r < n) ld_words<D>(a.in[g + r], v0 + (uint64_t)u * kRsagThreads, raw[u][r]);
     }
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
 #pragma unroll
-      for (int r = 0; r < kAnyGroup; ++r) {
+      for (int r = 0; r < G; ++r) {
         if (g + r >= n) break;
         float x[UE];
 #pragma unroll
@@ -232,7 +234,7 @@ __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint6
   }
 }
 
-template <int In, int Acc, int Out, int U>
+template <int In, int Acc, int Out, int U, int G>
 __global__ void __launch_bounds__(kRsagThreads) rsag_any_kernel(const RsagArgs a) {
   const int n = (int)a.nranks;
   for (uint32_t i = blockIdx.x; i < a.launch_tiles; i += gridDim.x) {
@@ -242,12 +244,12 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_any_kernel(const RsagArgs a
     const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
     const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
     if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
-      reduce_store_any<In, Acc, Out, U>(a, n, v0);
+      reduce_store_any<In, Acc, Out, U, G>(a, n, v0);
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
-        if (v < v_hi) reduce_store_any<In, Acc, Out, 1>(a, n, v);
+        if (v < v_hi) reduce_store_any<In, Acc, Out, 1, G>(a, n, v);
       }
     }
   }
@@ -321,17 +323,20 @@ static int rsag_any_wg_per_cu(int n, int tin) {
 }
 
 template <int In, int Acc, int Out>
-static void launch_any_typed(int mult, dim3 grid, const RsagArgs& a, hipStream_t s) {
+static void launch_any_typed(int n, int mult, dim3 grid, const RsagArgs& a, hipStream_t s) {
   constexpr int U = rsag_any_unroll(In, Out);
-  if constexpr (is_fp8(In)) {
-    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U>), grid, dim3(kRsagThreads), 0, s, a);
+  const dim3 block(kRsagThreads);
+  if (n > kAnyGroup) {
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroupWide>), grid, block, 0, s, a);
+  } else if constexpr (is_fp8(In)) {
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, 0, s, a);
   } else {
     if (mult == 4)
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 4 * U>), grid, dim3(kRsagThreads), 0, s, a);
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 4 * U, kAnyGroup>), grid, block, 0, s, a);
     else if (mult == 2)
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 2 * U>), grid, dim3(kRsagThreads), 0, s, a);
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 2 * U, kAnyGroup>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U>), grid, dim3(kRsagThreads), 0, s, a);
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, 0, s, a);
   }
 }
 
@@ -339,15 +344,24 @@ static void launch_any_typed(int mult, dim3 grid, const RsagArgs& a, hipStream_t
 // the same compile-time element sizes the kernels index with (Ty, Unit), so
 // the host plan and the kernel cannot disagree on how many elements a unit
 // or an input vector holds.
+// Chunk widths are rounded up to 256 bytes of input, so every chunk after the
+// first starts on a cache-line boundary and each wave's 1 KiB loads and
+// stores cover whole lines.  With the 16-byte rounding of the plain
+// definition, rank counts that do not divide the buffer into line multiples
+// (3, 6, 12, 24, ...) put most chunks off the line grid: measured on MI355X,
+// 6 x 64 MiB f16 157 -> 138 us, 12 x 64 MiB 342 -> 295 us, 24 x 64 MiB
+// 714 -> 608 us; power-of-two counts are unchanged.
+constexpr uint64_t kChunkAlignBytes = 256;
+
 template <int In, int Acc, int Out>
 static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs,
                                     void* const* outputs, hipStream_t stream) {
   const int n = p.nranks;
-  constexpr uint64_t vw = 16 / Ty<In>::size;  // chunk granularity: 16-byte input vectors
+  constexpr uint64_t vw = kChunkAlignBytes / Ty<In>::size;  // chunk granularity, elements
   constexpr uint64_t ue = Unit<In, Out>::UE;  // elements per unit (16-byte output vector)
-  static_assert(vw % ue == 0, "a unit must divide an input vector");
+  static_assert(vw % ue == 0, "a unit must divide the chunk granularity");
   const uint64_t count = p.count;
-  // Chunk width: ceil(count / N) rounded up to whole 16-byte input vectors.
+  // Chunk width: ceil(count / N) rounded up to whole 256-byte input blocks.
   const uint64_t per = (count + n - 1) / n;
   const uint64_t chunk_elems = (per + vw - 1) / vw * vw;
 
@@ -383,7 +397,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     const bool any_n = !valid_nranks(n) || small;
     a.nranks = (uint32_t)n;
     int mult = 1;
-    if (any_n && !small && !is_fp8(In)) {
+    if (any_n && !small && !is_fp8(In) && n <= kAnyGroup) {  // the wide-group kernel runs M = 1
       static const int m_env = [] {
         const char* v = getenv("MRR_RSAG_ANY_M");
         return v ? atoi(v) : 0;
@@ -418,7 +432,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     if (blocks == 0) blocks = 1;  // tail only
     const dim3 grid((uint32_t)blocks);
     if (any_n)
-      launch_any_typed<In, Acc, Out>(mult, grid, a, stream);
+      launch_any_typed<In, Acc, Out>(n, mult, grid, a, stream);
     else
       launch_vec_typed<In, Acc, Out>(n, grid, a, stream);
   } else {

@@ -102,10 +102,11 @@ typedef enum mrr_dtype {
  *   outputs[k][i] = round_out( x_0[i] + x_1[i] + ... + x_{nranks-1}[i] )
  * summed in rank order 0..nranks-1 starting from x_0 (so -0 sums stay -0).
  * The index space is split into nranks chunks of
- *   C = roundup(ceil(count / nranks), 16 / sizeof(input element))
- * elements (the last chunk may be short or empty); chunk r is rank r's
+ *   C = roundup(ceil(count / nranks), 256 / sizeof(input element))
+ * elements (the last chunks may be short or empty); chunk r is rank r's
  * reduce-scatter share, and its reduced values are written to all nranks
- * outputs (the all-gather).  The result does not depend on the partition.
+ * outputs (the all-gather).  The result does not depend on the partition;
+ * the 256-byte rounding keeps every chunk on the cache-line grid.
  *
  * mrr_allreduce_rsag: input type == output type == dtype (F32, F16, BF16 or
  *   FP8_E4M3B15), FP32 accumulation, every chunk.

@@ -20,6 +20,8 @@ TRIPLES = [("f32", "f32", "f32"), ("f16", "f32", "f16"), ("f16", "f16", "f16"),
            ("fp8", "f16", "fp8"), ("fp8", "f16", "f16"), ("fp8", "f16", "f32"),
            ("fp8", "fp8", "fp8"), ("fp8", "fp8", "f16"), ("fp8", "fp8", "f32")]
 VW = {"f32": 4, "f16": 8, "bf16": 8, "fp8": 16}
+# RS/AG chunk granularity in elements: 256 bytes of input.
+CHUNK_ALIGN = {"f32": 64, "f16": 128, "bf16": 128, "fp8": 256, "fp8fn": 256}
 
 
 def run(ins, t, acc, tout, rank=-1, outs=None, fill=0xA5):
@@ -100,14 +102,16 @@ def test_two_rank_bf16_one_mib():
     check_all(outs, oracle.allreduce([bits(x) for x in ins], "bf16", "f32"), "bf16", "2x1MiB")
 
 
-@pytest.mark.parametrize("n", [2, 8, 32])
-def test_rank_share_writes_only_its_chunk(n):
-    t, count = "f16", n * 1000 + 5
-    announce("rsag rank share", n)
+@pytest.mark.parametrize("n,count", [(2, 2005), (8, 8005), (32, 32005), (32, 1000), (16, 100003)])
+def test_rank_share_writes_only_its_chunk(n, count):
+    """rank=r writes exactly chunk r (256-byte rounded widths; with 32 ranks
+    of 1000 elements, ranks 8..31 own empty chunks and write nothing)."""
+    t = "f16"
+    announce("rsag rank share", n, count)
     ins = inputs_for(t, n, count, seed0=77)
     want = oracle.allreduce([bits(x) for x in ins], t, "f32", t)
     per = -(-count // n)
-    chunk = -(-per // VW[t]) * VW[t]
+    chunk = -(-per // CHUNK_ALIGN[t]) * CHUNK_ALIGN[t]
     for r in range(n):
         outs = run(ins, t, "f32", t, rank=r, fill=0x5A)
         lo, hi = min(r * chunk, count), min((r + 1) * chunk, count)
@@ -275,7 +279,7 @@ def test_rank_sweep_256mib_bf16_sampled(n):
     outs = [empty(t, count) for _ in range(n)]
     assert mrr.mrr_allreduce_rsag(ins, outs, count, t, n) == mrr.MRR_OK
     torch.cuda.synchronize()
-    idx = sample_indices(count, n, VW[t], np.random.default_rng(n))
+    idx = sample_indices(count, n, CHUNK_ALIGN[t], np.random.default_rng(n))
     sub_in = [bits(x[idx]) for x in ins]
     want = oracle.allreduce(sub_in, t, "f32")
     for k in range(n):
