@@ -120,7 +120,7 @@ int mrr_version(void) { return 10000; }
 size_t mrr_rank_buffer_pitch(size_t bytes_per_rank, int nranks) {
   if (bytes_per_rank == 0 || nranks < 1) return 0;
   const size_t page = 4096;
-  const size_t stagger = nranks >= 16 ? 2048 : 4096;
+  const size_t stagger = nranks >= 16 ? 3072 : 4096;
   return (bytes_per_rank + page - 1) / page * page + stagger;
 }
 

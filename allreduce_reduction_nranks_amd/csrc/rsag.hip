@@ -174,7 +174,8 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a
 }
 
 // Runtime rank count (1..32): the fallback for counts without a compiled
-// kernel.  Ranks are taken in groups of G (8 up to 8 ranks, else 16) behind
+// kernel.  Ranks are taken in groups of G (8 up to 8 ranks or with FP8 data or
+// accumulator, else 16) behind
 // wavefront-uniform bounds, in rank order, with the same unit structure as
 // reduce_store: all loads of a group are issued before its first add.
 constexpr int kAnyGroup = 8;
@@ -326,8 +327,12 @@ template <int In, int Acc, int Out>
 static void launch_any_typed(int n, int mult, dim3 grid, const RsagArgs& a, hipStream_t s) {
   constexpr int U = rsag_any_unroll(In, Out);
   const dim3 block(kRsagThreads);
-  if (n > kAnyGroup) {
-    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroupWide>), grid, block, 0, s, a);
+  // FP8 data or accumulators keep groups of 8 (as the compiled kernels do):
+  // their per-rank decode state for 16 ranks no longer stays in registers.
+  constexpr bool wide_ok = !is_fp8(In) && !is_fp8(Acc);
+  if (wide_ok && n > kAnyGroup) {
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, wide_ok ? kAnyGroupWide : kAnyGroup>), grid,
+                       block, 0, s, a);
   } else if constexpr (is_fp8(In)) {
     hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, 0, s, a);
   } else {

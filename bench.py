@@ -396,8 +396,8 @@ def bench_codec(args, torch, mrr, synth):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "custom", "codec"])
     ap.add_argument("--dir", default="dec16", choices=sorted(CODEC),
                     help="codec: direction (dec16/dec32 = E4M3B15 -> f16/f32, enc16/enc32 = back)")

@@ -282,12 +282,14 @@ mrr_status mrr_f32_to_fp8b15(const float* in, uint8_t* out, size_t n, void* stre
  * When the N same-size rank buffers of one side (inputs, or outputs) are
  * carved from one device allocation, consecutive buffers should be
  * mrr_rank_buffer_pitch(bytes, nranks) bytes apart: bytes rounded up to
- * 4 KiB plus a stagger of 4 KiB (nranks <= 8) or 2 KiB (nranks >= 16).
+ * 4 KiB plus a stagger of 4 KiB (nranks < 16) or 3 KiB (nranks >= 16).
  * Buffers spaced by a large power of two put the 2N equal-offset streams of
  * a reduction on the same DRAM channels; the stagger spreads them.  Measured
  * on MI355X with the RS/AG kernel, 8 x 64 MiB f16: 186.8 us with one
  * allocation per buffer, 180-181 us at this pitch, 205 us at an exact 64 MiB
- * pitch; 16 x 256 MiB bf16: 4 KiB stagger 5.06 TB/s, 2 KiB 5.53 TB/s.
+ * pitch.  At 16 and 32 ranks (64 and 256 MiB each, mean of three runs) a
+ * 3 KiB stagger gives 5.62 / 5.47 TB/s (N=16) and 5.28 / 5.10 TB/s (N=32),
+ * against 5.31 / 5.55 and 5.17 / 5.13 at 2 KiB and 4.97-5.38 at 4 KiB.
  * Advisory only: every entry point accepts any placement.  Returns 0 for
  * bytes == 0 or nranks < 1.
  * ------------------------------------------------------------------------ */

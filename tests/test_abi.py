@@ -197,7 +197,7 @@ def test_rank_buffer_pitch(lib):
     assert mrr.mrr_rank_buffer_pitch(0, 8) == 0 and mrr.mrr_rank_buffer_pitch(100, 0) == 0
     assert mrr.mrr_rank_buffer_pitch(1, 8) == 8192
     assert mrr.mrr_rank_buffer_pitch(64 * MiB, 8) == 64 * MiB + 4096
-    assert mrr.mrr_rank_buffer_pitch(64 * MiB, 16) == 64 * MiB + 2048
+    assert mrr.mrr_rank_buffer_pitch(64 * MiB, 16) == 64 * MiB + 3072
     assert mrr.mrr_rank_buffer_pitch(64 * MiB + 1, 2) == 64 * MiB + 8192
     for n in (2, 4, 8, 16, 32):
         for b in (4095, 4096, 4097, 12345, 256 * MiB):
