@@ -41,20 +41,28 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup
 // with the DRAM channel and bank mapping -- so each entry is the setting that
 // stayed near the best across buffer sizes rather than a formula.
 //   16-bit and 32-bit inputs: N=2 U=8 x2, N=4 U=4 x4, N=8 U=1 x6,
-//                             N=16 U=2 x2, N=32 U=1 x8 (workgroups per CU)
-//   FP8 inputs (E4M3B15 and OCP E4M3FN): U=4 for N=2, else 1, times 2 for
-//                             f16 and 4 for f32 outputs
-//                             (so a lane still loads 16 bytes per rank);
-//                             workgroups per CU: 4 (E4M3B15 out), 6 (E4M3FN
-//                             out, whose shorter body needs more waves in
-//                             flight), 3 (f16 out), 4 (f32 out).
+//                             N=16 U=1 x3, N=32 U=1 x8 (workgroups per CU;
+//                             N=16 from interleaved runs at 64 and 256 MiB,
+//                             +1.5 % over U=2 x2; at N=32 four per CU is 1 %
+//                             faster at 64 MiB but 19 % slower at 256 MiB)
+//   FP8 inputs (E4M3B15 and OCP E4M3FN): N=2: U=4 times 2 for f16 and 4 for
+//                             f32 outputs (a lane loads 16 bytes per rank),
+//                             4 workgroups per CU (3 for f16 out); N>2:
+//                             FP8 out U=1 x4 (E4M3FN out x6: its shorter
+//                             body needs more waves in flight), f16 out U=2
+//                             x3, f32 out U=1 x8 (a lane loads 4 bytes per
+//                             rank; 8 x 32 MiB E4M3B15 264.7 us against
+//                             265.9 us at U=4 x4).
 constexpr int rsag_unroll(int n, int tin, int tout) {
-  if (is_fp8(tin)) return (n == 2 ? 4 : 1) * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
-  return n == 2 ? 8 : n == 4 ? 4 : n == 16 ? 2 : 1;
+  if (is_fp8(tin)) {
+    if (n == 2) return 4 * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
+    return tout == kF16 ? 2 : 1;
+  }
+  return n == 2 ? 8 : n == 4 ? 4 : 1;
 }
 constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
-  if (is_fp8(tin)) return tout == kF16 ? 3 : tout == kFP8FN ? 6 : 4;
-  return n == 2 ? 2 : n == 4 ? 4 : n == 8 ? 6 : n == 16 ? 2 : 8;
+  if (is_fp8(tin)) return tout == kF16 ? 3 : tout == kFP8FN ? 6 : (tout == kF32 && n > 2) ? 8 : 4;
+  return n == 2 ? 2 : n == 4 ? 4 : n == 8 ? 6 : n == 16 ? 3 : 8;
 }
 // Ranks whose vectors are loaded together before they are added: all of them
 // up to 16 ranks; groups of 16 above that, and groups of 8 for FP8 inputs or

@@ -61,8 +61,10 @@ OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
 
 def table_unroll(n, t, tout):
     if t in ("fp8", "fp8fn"):
-        return (4 if n == 2 else 1) * {"f32": 4, "f16": 2}.get(tout, 1)
-    return {2: 8, 4: 4, 16: 2}.get(n, 1)
+        if n == 2:
+            return 4 * {"f32": 4, "f16": 2}.get(tout, 1)
+        return 2 if tout == "f16" else 1
+    return {2: 8, 4: 4}.get(n, 1)
 
 
 VEC_CASES = [(n, t, a, o) for (t, a, o) in TRIPLES + FN_TRIPLES
