@@ -254,3 +254,33 @@ def test_allpair_graph_replays_advance_flags():
         assert np.all(st.flags.cpu().numpy().view(np.uint32) == rep)
         for k in range(n):
             assert_bits_equal(bits(outs[k]), want, t, "replay %d out %d" % (rep, k))
+
+
+def test_flag_buffer_save_restore_and_recycle():
+    """The caller-owned flag buffer is the packet protocol's only persistent
+    state.  Saved to the host after three calls and restored into a fresh
+    buffer (with fresh zeroed scratch), the next call continues at flag 4;
+    a recycled buffer zeroed together with its scratch restarts at flag 1."""
+    n, t, count = 8, "f16", 6001
+    announce("packet flags save / restore")
+    st = PacketState(n, count, t)
+    outs = [empty(t, count, 0xEE) for _ in range(n)]
+    for flag in (1, 2, 3):
+        ins = inputs_for(t, n, count, seed0=4000 + flag, kind="uniform")
+        copies = [x.clone() for x in ins]
+        assert allpair(ins, outs, st, t, "f32") == mrr.MRR_OK
+        check_call(ins, outs, st, t, "f32", flag, copies, "call %d" % flag)
+    saved = st.flags.cpu().clone()
+    fresh = PacketState(n, count, t)
+    fresh.flags.copy_(saved.cuda())
+    ins = inputs_for(t, n, count, seed0=4100, kind="uniform")
+    copies = [x.clone() for x in ins]
+    assert allpair(ins, outs, fresh, t, "f32") == mrr.MRR_OK
+    check_call(ins, outs, fresh, t, "f32", 4, copies, "restored")
+    fresh.flags.zero_()
+    fresh.scratch.zero_()
+    torch.cuda.synchronize()
+    ins = inputs_for(t, n, count, seed0=4200, kind="uniform")
+    copies = [x.clone() for x in ins]
+    assert allpair(ins, outs, fresh, t, "f32") == mrr.MRR_OK
+    check_call(ins, outs, fresh, t, "f32", 1, copies, "recycled")
