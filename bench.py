@@ -213,15 +213,26 @@ def bench_rsag(args, torch, mrr, synth):
 
     compiled = n in (2, 4, 8, 16, 32)
 
+    rank = args.rank
+    if rank >= 0 and (not compiled or rank >= n):
+        raise SystemExit("--rank needs a compiled rank count (2, 4, 8, 16, 32) and 0 <= rank < N")
+
     def step():
         if compiled:
-            st = mrr.mrr_allreduce_rsag_ex(ins, outs, count, t, acc, tout, n, -1)
+            st = mrr.mrr_allreduce_rsag_ex(ins, outs, count, t, acc, tout, n, rank)
         else:  # rank counts without a compiled kernel: the runtime-N RS/AG
             st = mrr.mrr_allreduce(ins, outs, count, t, acc, n)
         if st != mrr.MRR_OK:
             raise mrr.MrrError(st)
 
-    alg_bytes = n * count * (ESIZE[t] + ESIZE[tout])
+    if rank < 0:
+        alg_bytes = n * count * (ESIZE[t] + ESIZE[tout])
+    else:  # one rank's share: chunk `rank` of every input, written to every output
+        gran = 256 // ESIZE[t]  # chunk widths are rounded to 256 bytes of input
+        per = -(-count // n)
+        chunk = -(-per // gran) * gran
+        elems = max(0, min(count, (rank + 1) * chunk) - min(count, rank * chunk))
+        alg_bytes = n * elems * (ESIZE[t] + ESIZE[tout])
     graph = use_graph(args, alg_bytes)
     eager_us = None
     if graph:
@@ -232,7 +243,7 @@ def bench_rsag(args, torch, mrr, synth):
     sep_us = None
     if args.layout == "pitch":
         def step_sep():
-            st = mrr.mrr_allreduce_rsag_ex(ins_sep, outs_sep, count, t, acc, tout, n, -1) \
+            st = mrr.mrr_allreduce_rsag_ex(ins_sep, outs_sep, count, t, acc, tout, n, rank) \
                 if compiled else mrr.mrr_allreduce(ins_sep, outs_sep, count, t, acc, n)
             if st != mrr.MRR_OK:
                 raise mrr.MrrError(st)
@@ -275,6 +286,14 @@ def bench_rsag(args, torch, mrr, synth):
     result["config"]["timing"] = TIMING_GRAPH if graph else TIMING_EAGER
     if eager_us is not None:
         result["config"]["eager_us_per_call"] = round(eager_us, 2)
+    if rank >= 0:
+        # One rank's share (the per-GPU work of the sharded layout); the
+        # counter summaries and the oracle baseline cover whole calls only.
+        result["config"]["workload"] += (", rank %d's share only (chunk %d of every input, "
+                                         "written to all %d outputs)" % (rank, rank, n))
+        result["config"]["rank"] = rank
+        result["roofline"]["traffic"] = None
+        return result
     if args.cpu_baseline:
         sample = min(count, args.cpu_sample)
         result["cpu_baseline"] = cpu_baseline_rsag(ins, t, acc, tout, sample)
@@ -421,6 +440,8 @@ def main():
                     help="elements per rank the CPU oracle baseline reduces")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-copy-ceiling", dest="copy_ceiling", action="store_false")
+    ap.add_argument("--rank", type=int, default=-1,
+                    help="RS/AG configs: time only this rank's share (chunk `rank`), -1 = all")
     ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
                     help="time a HIP graph of the K calls (auto: when a call moves < 64 MiB)")
     args = ap.parse_args()
