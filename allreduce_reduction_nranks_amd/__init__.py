@@ -58,6 +58,7 @@ def load_library() -> ctypes.CDLL:
         sigs = {
             "mrr_allreduce_rsag": ([pp, pp, sz, i, i, vp], i),
             "mrr_allreduce_rsag_ex": ([pp, pp, sz, i, i, i, i, i, vp], i),
+            "mrr_allreduce_rsag_dual": ([pp, pp, pp, sz, i, i, i, i, vp], i),
             "mrr_packet_scratch_bytes": ([sz, i, i], sz),
             "mrr_packet_flag_bytes": ([i], sz),
             "mrr_allreduce_packet": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, vp], i),
@@ -160,6 +161,13 @@ def mrr_allreduce_rsag_ex(inputs, outputs, count, dtype_in, accum, dtype_out, nr
     return load_library().mrr_allreduce_rsag_ex(_ptrs(inputs), _ptrs(outputs), count,
                                                 _dt(dtype_in), _dt(accum), _dt(dtype_out),
                                                 nranks, rank, _stream(stream))
+
+
+def mrr_allreduce_rsag_dual(inputs, outputs, outputs2, count, dtype_in, accum, nranks, rank=-1,
+                            stream=None) -> int:
+    return load_library().mrr_allreduce_rsag_dual(_ptrs(inputs), _ptrs(outputs), _ptrs(outputs2),
+                                                  count, _dt(dtype_in), _dt(accum), nranks, rank,
+                                                  _stream(stream))
 
 
 def mrr_packet_scratch_bytes(count, dtype, nranks) -> int:

@@ -162,6 +162,33 @@ mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs
                    stream, false);
 }
 
+mrr_status mrr_allreduce_rsag_dual(const void* const* inputs, void* const* outputs,
+                                   void* const* outputs2, size_t count, mrr_dtype in,
+                                   mrr_dtype accum, int nranks, int rank, void* stream) {
+  static const char* fn = "mrr_allreduce_rsag_dual";
+  if (!valid_nranks(nranks)) return refuse(MRR_EUNSUPPORTED, fn, "nranks not in {2,4,8,16,32}");
+  if (rank < -1 || rank >= nranks) return refuse(MRR_EINVAL, fn, "rank outside [-1, nranks)");
+  if (!inputs || !outputs || !outputs2) return refuse(MRR_EINVAL, fn, "null pointer array");
+  const int tin = (int)in;
+  const int tacc = accum == MRR_AUTO ? tin : (int)accum;
+  if (!rsag_dual_supported(tin, tacc)) return refuse(MRR_EUNSUPPORTED, fn, "type combination");
+  if (count == 0) return MRR_OK;
+  if (count > ((uint64_t)1 << 39)) return refuse(MRR_EINVAL, fn, "count too large for one call");
+  for (int r = 0; r < nranks; ++r) {
+    if (!inputs[r] || !outputs[r] || !outputs2[r]) return refuse(MRR_EINVAL, fn, "null buffer");
+    if (!aligned(inputs[r], 16) || !aligned(outputs[r], 16) || !aligned(outputs2[r], 16))
+      return refuse(MRR_EALIGN, fn, "every buffer must be 16-byte aligned");
+  }
+  // outputs2[k] may be exactly inputs[k] (same type and size); the f16
+  // outputs may overlap nothing.
+  if (bad_overlap(inputs, count, outputs2, count, nranks) ||
+      bad_overlap(inputs, count, outputs, 2 * count, nranks) ||
+      bad_overlap((const void* const*)outputs2, count, outputs, 2 * count, nranks))
+    return refuse(MRR_EOVERLAP, fn, "an output overlaps another buffer");
+  RsagPlan plan{nranks, tin, tacc, kF16, count, rank, true};
+  return hip_status(launch_rsag_dual(plan, inputs, outputs, outputs2, (hipStream_t)stream), fn);
+}
+
 mrr_status mrr_allreduce_rsag(const void* const* inputs, void* const* outputs, size_t count,
                               mrr_dtype dtype, int nranks, void* stream) {
   return mrr_allreduce_rsag_ex(inputs, outputs, count, dtype, MRR_F32, MRR_AUTO, nranks, -1,

@@ -27,19 +27,6 @@ template <> struct CodecShape<kDecF32> { static constexpr int V = 4, DI = 1, DO 
 template <> struct CodecShape<kEncF16> { static constexpr int V = 8, DI = 4, DO = 2; };
 template <> struct CodecShape<kEncF32> { static constexpr int V = 4, DI = 4, DO = 1; };
 
-// Stores D words as unit `unit` of a buffer, non-temporal.
-template <int D> __device__ __forceinline__ void st_words(void* base, uint64_t unit, const uint32_t* w) {
-  typedef typename WordsT<D>::type Vt;
-  Vt v;
-  if constexpr (D == 1) {
-    v = w[0];
-  } else {
-#pragma unroll
-    for (int j = 0; j < D; ++j) v[j] = w[j];
-  }
-  __builtin_nontemporal_store(v, reinterpret_cast<Vt*>(base) + unit);
-}
-
 template <int Dir> __device__ __forceinline__ void convert_unit(const uint32_t* in, uint32_t* out) {
   if constexpr (Dir == kDecF16) {
 #pragma unroll

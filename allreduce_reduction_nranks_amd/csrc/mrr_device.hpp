@@ -253,6 +253,19 @@ template <int D> __device__ __forceinline__ void ld_words(const void* base, uint
   }
 }
 
+// Stores D words as unit `unit` of a buffer (D-word units), non-temporal.
+template <int D> __device__ __forceinline__ void st_words(void* base, uint64_t unit, const uint32_t* w) {
+  typedef typename WordsT<D>::type V;
+  V v;
+  if constexpr (D == 1) {
+    v = w[0];
+  } else {
+#pragma unroll
+    for (int j = 0; j < D; ++j) v[j] = w[j];
+  }
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(base) + unit);
+}
+
 // Elements of type T in one 32-bit word, widened to f32.
 template <int T> __device__ __forceinline__ void decode_word(uint32_t w, float* x) {
   if constexpr (T == kF32) {
@@ -379,6 +392,29 @@ template <int T> __device__ __forceinline__ u32x4 encode16(const float* x) {
     }
   }
   return v;
+}
+
+// 8 f32 values -> two words of FP8 codes of type T (E4M3B15 or E4M3FN), one
+// rounding each.  For E4M3B15, `exact` selects the bit-arithmetic encoder
+// (units holding inf / NaN); otherwise the hardware converts.
+template <int T> __device__ __forceinline__ void encode8_fp8(const float* x, bool exact, uint32_t* w) {
+  static_assert(T == kFP8 || T == kFP8FN, "FP8 output types only");
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if constexpr (T == kFP8FN) {
+      w[j] = encode2_fp8fn<true>(x[4 * j + 2], x[4 * j + 3], encode2_fp8fn<false>(x[4 * j], x[4 * j + 1], 0u));
+    } else {
+      if (exact) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v |= f32_to_fp8(x[4 * j + b]) << (8 * b);
+        w[j] = v;
+      } else {
+        w[j] = encode2_fp8_hw<true>(x[4 * j + 2], x[4 * j + 3],
+                                    encode2_fp8_hw<false>(x[4 * j], x[4 * j + 1], 0u));
+      }
+    }
+  }
 }
 
 }  // namespace mrr

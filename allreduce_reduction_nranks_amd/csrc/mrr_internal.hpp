@@ -29,6 +29,13 @@ struct RsagArgs {
   uint32_t pad;
 };
 
+// RS/AG with a second output set: FP8 inputs reduced once, written as f16 to
+// `base.out` and re-encoded to the input's FP8 type in `out2`.
+struct RsagDualArgs {
+  RsagArgs base;
+  void* out2[kMaxRanks];
+};
+
 // Element-wise kernel arguments (pointers not 16-byte aligned).
 struct RsagScalarArgs {
   const void* in[kMaxRanks];
@@ -53,6 +60,12 @@ bool rsag_types_supported(int tin, int tacc, int tout);
 
 hipError_t launch_rsag(const RsagPlan& plan, const void* const* inputs, void* const* outputs,
                        hipStream_t stream);
+
+// Dual-output RS/AG (plan.tout is F16, the second outputs take plan.tin):
+// FP8 inputs only, compiled rank counts, every pointer 16-byte aligned.
+bool rsag_dual_supported(int tin, int tacc);
+hipError_t launch_rsag_dual(const RsagPlan& plan, const void* const* inputs, void* const* outputs,
+                            void* const* outputs2, hipStream_t stream);
 bool rsag_supported(int nranks, int tin, int tacc, int tout);
 
 // ---- LL packets -------------------------------------------------------------

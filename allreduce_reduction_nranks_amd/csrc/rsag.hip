@@ -72,12 +72,15 @@ constexpr int rsag_group(int n, int tin, int tacc) {
   return (is_fp8(tin) || is_fp8(tacc)) ? (n < 8 ? n : 8) : (n < 16 ? n : 16);
 }
 
-template <int In, int Acc, int Out>
+// Out2 != 0: the same sum is also written, as type Out2, to out2[0..n-1].
+template <int In, int Acc, int Out, int Out2 = 0>
 __device__ __forceinline__ void reduce_elem(const void* const* in, void* const* out, int n,
-                                            uint64_t i) {
+                                            uint64_t i, void* const* out2 = nullptr) {
   float acc = round_acc<Acc>(load_elem<In>(in[0], i));
   for (int r = 1; r < n; ++r) acc = round_acc<Acc>(acc + load_elem<In>(in[r], i));
   for (int k = 0; k < n; ++k) store_elem<Out>(out[k], i, acc);
+  if constexpr (Out2 != 0)
+    for (int k = 0; k < n; ++k) store_elem<Out2>(out2[k], i, acc);
 }
 
 // A unit is one 16-byte output vector: UE = 16 / size(Out) elements, whose
@@ -101,8 +104,12 @@ template <int In, int Out> struct Unit {
 // hold an exponent-15 code (inf / NaN) marks that unit `special`, fixes
 // those values, and rounds / encodes that unit with the exact bit arithmetic
 // instead of the converts, which are only exact for finite data.
-template <int N, int In, int Acc, int Out, int UU, int G>
-__device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
+//
+// Out2 != 0 (FP8 types only, with Out = f16): each unit's 8 sums are also
+// encoded to Out2 and stored, 8 bytes per lane, to out2[0..N-1].
+template <int N, int In, int Acc, int Out, int UU, int G, int Out2 = 0>
+__device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
+                                             void* const* out2 = nullptr) {
   constexpr int UE = Unit<In, Out>::UE;
   constexpr int D = Unit<In, Out>::D;
   constexpr int EPW = Unit<In, Out>::EPW;
@@ -153,11 +160,19 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0) {
     else o = encode16<Out>(acc[u]);
 #pragma unroll
     for (int k = 0; k < N; ++k) st_stream(a.out[k], v, o);
+    if constexpr (Out2 != 0) {
+      static_assert(UE == 8, "second FP8 output needs 8-element units");
+      uint32_t w2[2];
+      encode8_fp8<Out2>(acc[u], special[u], w2);
+#pragma unroll
+      for (int k = 0; k < N; ++k) st_words<2>(out2[k], v, w2);
+    }
   }
 }
 
-template <int N, int In, int Acc, int Out, int U>
-__global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a) {
+// The persistent tile loop shared by the single- and dual-output kernels.
+template <int N, int In, int Acc, int Out, int U, int Out2>
+__device__ __forceinline__ void rsag_vec_body(const RsagArgs& a, void* const* out2) {
   constexpr int G = rsag_group(N, In, Acc);
   for (uint32_t i = blockIdx.x; i < a.launch_tiles; i += gridDim.x) {
     const uint32_t chunk_rel = i / a.tiles_per_chunk;
@@ -166,19 +181,30 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a
     const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
     const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
     if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
-      reduce_store<N, In, Acc, Out, U, G>(a, v0);
+      reduce_store<N, In, Acc, Out, U, G, Out2>(a, v0, out2);
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
-        if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G>(a, v);
+        if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G, Out2>(a, v, out2);
       }
     }
   }
   // Elements past the last whole vector (count % VW of them, fewer than one
   // wave) go to the last workgroup, one per lane.
   if (a.tail_count != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < a.tail_count)
-    reduce_elem<In, Acc, Out>(a.in, a.out, N, a.tail_begin + threadIdx.x);
+    reduce_elem<In, Acc, Out, Out2>(a.in, a.out, N, a.tail_begin + threadIdx.x, out2);
+}
+
+template <int N, int In, int Acc, int Out, int U>
+__global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a) {
+  rsag_vec_body<N, In, Acc, Out, U, 0>(a, nullptr);
+}
+
+// FP8 inputs, f16 outputs plus the FP8 re-encode of the same sums.
+template <int N, int In, int Acc, int U>
+__global__ void __launch_bounds__(kRsagThreads) rsag_dual_kernel(const RsagDualArgs d) {
+  rsag_vec_body<N, In, Acc, kF16, U, In>(d.base, d.out2);
 }
 
 // Runtime rank count (1..32): the fallback for counts without a compiled
@@ -366,6 +392,47 @@ static void launch_any_typed(int n, int mult, dim3 grid, const RsagArgs& a, hipS
 // 714 -> 608 us; power-of-two counts are unchanged.
 constexpr uint64_t kChunkAlignBytes = 256;
 
+// Chunk and tile geometry of a launch: chunks of ceil(count / N) elements
+// rounded up to vw, units of ue elements, tiles of tile_units units; every
+// chunk (rank < 0) or chunk `rank` only.
+static void rsag_geometry(const RsagPlan& p, uint64_t vw, uint64_t ue, uint64_t tile_units,
+                          RsagArgs& a) {
+  const uint64_t n = (uint64_t)p.nranks;
+  const uint64_t per = (p.count + n - 1) / n;
+  const uint64_t chunk_elems = (per + vw - 1) / vw * vw;
+  a.chunk_vecs = chunk_elems / ue;
+  a.total_vecs = p.count / ue;
+  a.tail_begin = a.total_vecs * ue;
+  const uint32_t tail = (uint32_t)(p.count - a.tail_begin);
+  const uint64_t tail_chunk = a.chunk_vecs ? a.total_vecs / a.chunk_vecs : 0;
+  a.nranks = (uint32_t)n;
+  a.tiles_per_chunk = (uint32_t)((a.chunk_vecs + tile_units - 1) / tile_units);
+  if (p.rank < 0) {
+    a.first_chunk = 0;
+    a.tail_count = tail;
+    a.launch_tiles = (uint32_t)n * a.tiles_per_chunk;
+  } else {
+    a.first_chunk = (uint32_t)p.rank;
+    a.tail_count = tail_chunk == (uint64_t)p.rank ? tail : 0;
+    a.launch_tiles = a.tiles_per_chunk;
+  }
+}
+
+// Persistent grid: wpc workgroups per CU (MRR_RSAG_WPC overrides), at most
+// one per tile, at least one (a tail-only launch).
+static dim3 rsag_grid(int wpc, uint32_t launch_tiles) {
+  static const int wpc_env = [] {
+    const char* v = getenv("MRR_RSAG_WPC");
+    return v ? atoi(v) : 0;
+  }();
+  if (wpc_env > 0) wpc = wpc_env;
+  uint64_t blocks = (uint64_t)device_cu_count(-1) * (uint64_t)wpc;
+  if (blocks == 0) blocks = 1024;
+  if (blocks > launch_tiles) blocks = launch_tiles;
+  if (blocks == 0) blocks = 1;
+  return dim3((uint32_t)blocks);
+}
+
 template <int In, int Acc, int Out>
 static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs,
                                     void* const* outputs, hipStream_t stream) {
@@ -384,11 +451,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
       a.in[r] = inputs[r];
       a.out[r] = outputs[r];
     }
-    a.chunk_vecs = chunk_elems / ue;
-    a.total_vecs = count / ue;
-    a.tail_begin = a.total_vecs * ue;
-    const uint32_t tail = (uint32_t)(count - a.tail_begin);
-    const uint64_t tail_chunk = a.chunk_vecs ? a.total_vecs / a.chunk_vecs : 0;
+    rsag_geometry(p, vw, ue, (uint64_t)kRsagThreads * rsag_unroll(n, In, Out), a);
     // Small calls: when the table's U would leave fewer than 2 tiles per CU,
     // CUs sit idle; the runtime-N kernel at one unit group per lane spreads
     // the same work over U times more workgroups (measured under HIP-graph
@@ -402,13 +465,9 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     }();
     bool small = false;
     if (valid_nranks(n) && n <= kAnyGroup && small_ok &&
-        rsag_unroll(n, In, Out) > rsag_any_unroll(In, Out)) {
-      const uint64_t vec_tile = (uint64_t)kRsagThreads * rsag_unroll(n, In, Out);
-      const uint64_t vec_tiles = (uint64_t)(p.rank < 0 ? n : 1) * ((a.chunk_vecs + vec_tile - 1) / vec_tile);
-      small = vec_tiles < 2 * (uint64_t)(device_cu_count(-1) > 0 ? device_cu_count(-1) : 256);
-    }
+        rsag_unroll(n, In, Out) > rsag_any_unroll(In, Out))
+      small = a.launch_tiles < 2 * (uint64_t)(device_cu_count(-1) > 0 ? device_cu_count(-1) : 256);
     const bool any_n = !valid_nranks(n) || small;
-    a.nranks = (uint32_t)n;
     int mult = 1;
     if (any_n && !small && !is_fp8(In) && n <= kAnyGroup) {  // the wide-group kernel runs M = 1
       static const int m_env = [] {
@@ -417,33 +476,11 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
       }();
       mult = (m_env == 1 || m_env == 2 || m_env == 4) ? m_env : rsag_any_multiplier(n);
     }
-    const uint64_t tile_vecs =
-        (uint64_t)kRsagThreads * (any_n ? rsag_any_unroll(In, Out) * mult : rsag_unroll(n, In, Out));
-    a.tiles_per_chunk = (uint32_t)((a.chunk_vecs + tile_vecs - 1) / tile_vecs);
-    uint32_t nchunks;
-    if (p.rank < 0) {
-      a.first_chunk = 0;
-      nchunks = (uint32_t)n;
-      a.tail_count = tail;
-    } else {
-      a.first_chunk = (uint32_t)p.rank;
-      nchunks = 1;
-      a.tail_count = tail_chunk == (uint64_t)p.rank ? tail : 0;
-    }
-    a.launch_tiles = nchunks * a.tiles_per_chunk;
+    if (any_n)
+      rsag_geometry(p, vw, ue, (uint64_t)kRsagThreads * rsag_any_unroll(In, Out) * mult, a);
     if (a.launch_tiles == 0 && a.tail_count == 0) return hipSuccess;
-    // Persistent grid: wg_per_cu workgroups per CU (MRR_RSAG_WPC overrides).
-    int wpc = small ? 8 : any_n ? rsag_any_wg_per_cu(n, In) : rsag_wg_per_cu(n, In, Out);
-    static const int wpc_env = [] {
-      const char* v = getenv("MRR_RSAG_WPC");
-      return v ? atoi(v) : 0;
-    }();
-    if (wpc_env > 0) wpc = wpc_env;
-    uint64_t blocks = (uint64_t)device_cu_count(-1) * (uint64_t)wpc;
-    if (blocks == 0) blocks = 1024;
-    if (blocks > a.launch_tiles) blocks = a.launch_tiles;
-    if (blocks == 0) blocks = 1;  // tail only
-    const dim3 grid((uint32_t)blocks);
+    const dim3 grid = rsag_grid(small ? 8 : any_n ? rsag_any_wg_per_cu(n, In) : rsag_wg_per_cu(n, In, Out),
+                                a.launch_tiles);
     if (any_n)
       launch_any_typed<In, Acc, Out>(n, mult, grid, a, stream);
     else
@@ -480,6 +517,58 @@ hipError_t launch_rsag(const RsagPlan& p, const void* const* inputs, void* const
   MRR_RSAG_TRIPLES(MRR_DISPATCH)
 #undef MRR_DISPATCH
   return hipErrorInvalidValue;  // callers check rsag_types_supported first
+}
+
+#define MRR_RSAG_DUAL_PAIRS(X) \
+  X(kFP8, kF32) X(kFP8, kF16) X(kFP8, kFP8) X(kFP8FN, kF32) X(kFP8FN, kF16) X(kFP8FN, kFP8FN)
+
+bool rsag_dual_supported(int tin, int tacc) {
+#define MRR_MATCH(I, A) if (tin == I && tacc == A) return true;
+  MRR_RSAG_DUAL_PAIRS(MRR_MATCH)
+#undef MRR_MATCH
+  return false;
+}
+
+// Dual output: units of 8 elements (one 16-byte f16 vector and 8 FP8 codes
+// per lane), with the FP8 -> f16 launch shape.
+template <int In, int Acc>
+static hipError_t launch_rsag_dual_typed(const RsagPlan& p, const void* const* inputs,
+                                         void* const* outputs, void* const* outputs2,
+                                         hipStream_t stream) {
+  const int n = p.nranks;
+  RsagDualArgs d = {};
+  for (int r = 0; r < n; ++r) {
+    d.base.in[r] = inputs[r];
+    d.base.out[r] = outputs[r];
+    d.out2[r] = outputs2[r];
+  }
+  constexpr uint64_t vw = kChunkAlignBytes / Ty<In>::size;
+  constexpr uint64_t ue = Unit<In, kF16>::UE;
+  rsag_geometry(p, vw, ue, (uint64_t)kRsagThreads * rsag_unroll(n, In, kF16), d.base);
+  if (d.base.launch_tiles == 0 && d.base.tail_count == 0) return hipSuccess;
+  const dim3 grid = rsag_grid(rsag_wg_per_cu(n, In, kF16), d.base.launch_tiles);
+  const dim3 block(kRsagThreads);
+  switch (n) {
+#define MRR_CASE(N)                                                                          \
+  case N:                                                                                    \
+    hipLaunchKernelGGL((rsag_dual_kernel<N, In, Acc, rsag_unroll(N, In, kF16)>), grid, block, 0, \
+                       stream, d);                                                           \
+    break;
+    MRR_CASE(2) MRR_CASE(4) MRR_CASE(8) MRR_CASE(16) MRR_CASE(32)
+#undef MRR_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rsag_dual(const RsagPlan& p, const void* const* inputs, void* const* outputs,
+                            void* const* outputs2, hipStream_t stream) {
+  if (!p.vector || !valid_nranks(p.nranks)) return hipErrorInvalidValue;
+#define MRR_DISPATCH(I, A) \
+  if (p.tin == I && p.tacc == A) return launch_rsag_dual_typed<I, A>(p, inputs, outputs, outputs2, stream);
+  MRR_RSAG_DUAL_PAIRS(MRR_DISPATCH)
+#undef MRR_DISPATCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mrr

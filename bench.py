@@ -348,6 +348,70 @@ def bench_packet(args, torch, mrr, synth):
     }
 
 
+def bench_dual(args, torch, mrr, synth):
+    """FP8 workload with both outputs from one pass: 8 ranks x 32 MiB codes,
+    fp32 accumulation, f16 outputs and the FP8 re-encode (mrr_allreduce_rsag_dual)."""
+    n, per_rank = 8, 32 * MiB
+    t = "fp8fn" if args.fp8 == "e4m3fn" else "fp8"
+    acc, count = "f32", per_rank
+    gen_dev = "cuda"
+    log("config c4 dual", "n", n, "type", t, "count", count)
+    src = [x.to("cuda") for x in synth.rank_inputs("fp8codes", t, n, count, args.seed0, device=gen_dev)]
+    _, ins = mrr.alloc_rank_buffers(n, count, t)
+    for dst, x in zip(ins, src):
+        dst.copy_(x)
+    del src
+    _, o16 = mrr.alloc_rank_buffers(n, count, "f16")
+    _, o8 = mrr.alloc_rank_buffers(n, count, t)
+    torch.cuda.synchronize()
+
+    def step():
+        st = mrr.mrr_allreduce_rsag_dual(ins, o16, o8, count, t, acc, n, -1)
+        if st != mrr.MRR_OK:
+            raise mrr.MrrError(st)
+
+    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    alg_bytes = n * count * (1 + 2 + 1)
+    value = alg_bytes / (wall_ms * 1e-3) / 1e9
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    key = "rsag_dual_8x32MiB_%s" % t
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded, rank r drawn with seed %d + r)" % args.seed0,
+        "config": {"workload": "RS/AG allreduce, 8 ranks x 32 MiB FP8 %s finite codes, fp32 "
+                               "accumulation, f16 outputs and the FP8 re-encode from one pass"
+                               % ("E4M3B15" if t == "fp8" else "OCP E4M3FN"),
+                   "nranks": n, "bytes_per_rank": count, "count": count, "in": t, "accum": acc,
+                   "out": "f16 + %s" % t, "algorithmic_bytes_per_call": alg_bytes,
+                   "kernel_us": round(kern_ms * 1e3, 2),
+                   "pct_of_hbm_peak": round(100 * value / PEAK_GBPS, 2),
+                   "layout": "one allocation per side, rank buffers mrr_rank_buffer_pitch() apart",
+                   "timing": TIMING_EAGER},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": measured_traffic(key)},
+    }
+    if args.copy_ceiling:
+        result["config"]["copy_ceiling_gbps"] = round(copy_ceiling(torch, n * count), 2)
+    if args.cpu_baseline:
+        import oracle
+        sample = min(count, args.cpu_sample)
+        sub = [synth.to_bits_numpy(x[:sample]) for x in ins]
+        oracle.default()
+        t0 = time.perf_counter()
+        oracle.allreduce_all(sub, t, acc, "f16")
+        oracle.allreduce_all(sub, t, acc, t)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(n * sample * 4 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "first %d elements of each of the %d ranks (%.1f%% of the workload), both "
+                      "output sets written, one thread, %.1f s" % (sample, n, 100.0 * sample / count, dt)}
+    return result
+
+
 CODEC = {  # --dir: (entry point, input type, output type)
     "dec16": ("mrr_fp8b15_to_f16", "fp8", "f16"), "dec32": ("mrr_fp8b15_to_f32", "fp8", "f32"),
     "enc16": ("mrr_f16_to_fp8b15", "f16", "fp8"), "enc32": ("mrr_f32_to_fp8b15", "f32", "fp8")}
@@ -423,8 +487,9 @@ def main():
     ap.add_argument("--dtype", default="f16", choices=["f32", "f16", "bf16", "fp8", "fp8fn"],
                     help="custom: type (fp8 = E4M3B15, fp8fn = OCP E4M3FN)")
     ap.add_argument("--nranks", type=int, default=8, help="c5: rank count")
-    ap.add_argument("--out", default="f16", choices=["f16", "fp8", "f32"],
-                    help="c4 / custom FP8: output type (fp8 = the input's FP8 format)")
+    ap.add_argument("--out", default="f16", choices=["f16", "fp8", "f32", "dual"],
+                    help="c4 / custom FP8: output type (fp8 = the input's FP8 format; c4 dual = "
+                         "f16 outputs and the FP8 re-encode from one pass)")
     ap.add_argument("--fp8", default="e4m3b15", choices=["e4m3b15", "e4m3fn"],
                     help="c4: FP8 input format")
     ap.add_argument("--size", type=int, default=1024, help="c3 / custom: KiB per rank")
@@ -463,6 +528,8 @@ def main():
         result = bench_packet(args, torch, mrr, synth)
     elif args.config == "codec":
         result = bench_codec(args, torch, mrr, synth)
+    elif args.config == "c4" and args.out == "dual":
+        result = bench_dual(args, torch, mrr, synth)
     else:
         result = bench_rsag(args, torch, mrr, synth)
     print(json.dumps(result), flush=True)

@@ -139,6 +139,34 @@ mrr_status mrr_allreduce_rsag_ex(const void* const* inputs, void* const* outputs
                                  int rank, void* stream);
 
 /* --------------------------------------------------------------------------
+ * RS/AG allreduce of FP8 inputs with two outputs from one pass ("MSCCL++
+ * commit history for /src", FP8 accumulation entry: FP8 data reduced with
+ * higher-precision accumulation; the FP8 workloads emit an f16 result and an
+ * FP8 re-encode of the same sums).
+ *
+ * Same sum, partition and rank semantics as mrr_allreduce_rsag_ex with
+ * in = FP8_E4M3B15 or FP8_E4M3FN; every reduced value is written twice:
+ *   outputs[k][i]  = round_f16(sum)           (count f16 elements)
+ *   outputs2[k][i] = round_in(sum)            (count codes of the input type,
+ *                                              RNE, saturating as in the
+ *                                              conversions above)
+ * both rounded once from the accumulator (so outputs2 is not a rounding of
+ * outputs).  Equivalent to two mrr_allreduce_rsag_ex calls (out = F16, then
+ * out = in) but the inputs are read once: N*count*(1 + 2 + 1) bytes moved
+ * instead of N*count*(1 + 2) + N*count*(1 + 1).
+ *   accum  AUTO (= in) | F32 | F16
+ * Buffers: every inputs[r], outputs[k] and outputs2[k] 16-byte aligned
+ * (MRR_EALIGN otherwise); outputs2[k] may be exactly inputs[k]; any other
+ * overlap of an output gives MRR_EOVERLAP.
+ * Errors: MRR_EUNSUPPORTED for nranks not in {2,4,8,16,32} or another type;
+ * MRR_EINVAL for null arrays/pointers or rank outside [-1, nranks);
+ * MRR_EHIP when the launch fails.
+ * ------------------------------------------------------------------------ */
+mrr_status mrr_allreduce_rsag_dual(const void* const* inputs, void* const* outputs,
+                                   void* const* outputs2, size_t count, mrr_dtype in,
+                                   mrr_dtype accum, int nranks, int rank, void* stream);
+
+/* --------------------------------------------------------------------------
  * LL-packet allpair allreduce (commit history: allreduce_allpair_packet fix;
  * default flag buffer entry).
  *

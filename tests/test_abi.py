@@ -236,3 +236,35 @@ def test_packet_rsag_sizes_and_checks(lib):
     assert f(ins[:3], outs[:3], fake(200), need, fake(300), 4096, "f16", "f32", 3, 10, 0, 0, 0, 0) == mrr.MRR_EUNSUPPORTED
     assert f(ins, outs, fake(200), need, fake(300), 4096, "f16", "f32", 8, 10, 0, 0, 96, 0) == mrr.MRR_EINVAL
     assert f(ins, outs, fake(200), need, fake(300), 0, "f16", "f32", 8, 10, 0, 0, 0, 0) == mrr.MRR_OK
+
+
+def test_rsag_dual_checks(lib):
+    """mrr_allreduce_rsag_dual: refusals before any launch."""
+    n = 8
+    ins = [fake(r) for r in range(n)]
+    o16 = [fake(64 + r) for r in range(n)]
+    o8 = [fake(128 + r) for r in range(n)]
+    f = mrr.mrr_allreduce_rsag_dual
+    assert f(ins, o16, o8, 0, "fp8", "f32", n, stream=0) == mrr.MRR_OK  # nothing to do
+    assert f(ins[:3], o16[:3], o8[:3], 1024, "fp8", "f32", 3, stream=0) == mrr.MRR_EUNSUPPORTED
+    for t, acc in (("f16", "f32"), ("bf16", "f32"), ("fp8", "bf16"), ("fp8fn", "fp8"),
+                   ("fp8", "fp8fn")):
+        assert f(ins, o16, o8, 1024, t, acc, n, stream=0) == mrr.MRR_EUNSUPPORTED, (t, acc)
+    assert f(ins, o16, o8, 1024, "fp8", "f32", n, rank=8, stream=0) == mrr.MRR_EINVAL
+    assert f(ins, o16, o8, 1024, "fp8", "f32", n, rank=-2, stream=0) == mrr.MRR_EINVAL
+    assert lib.mrr_allreduce_rsag_dual(None, None, None, 16, 4, 1, n, -1, None) == mrr.MRR_EINVAL
+    bad = list(o8)
+    bad[2] = 0
+    assert f(ins, o16, bad, 1024, "fp8", "f32", n, stream=0) == mrr.MRR_EINVAL
+    bad = list(o8)
+    bad[5] = fake(128 + 5, off=8)  # 8-byte aligned only
+    assert f(ins, o16, bad, 1024, "fp8", "f32", n, stream=0) == mrr.MRR_EALIGN
+    bad = list(o16)
+    bad[1] = ins[1]  # an f16 output on top of an input
+    assert f(ins, bad, o8, 1024, "fp8", "f32", n, stream=0) == mrr.MRR_EOVERLAP
+    bad = list(o8)
+    bad[3] = o16[3] + 512  # an FP8 output inside an f16 output
+    assert f(ins, o16, bad, 1024, "fp8", "f32", n, stream=0) == mrr.MRR_EOVERLAP
+    bad = list(o8)
+    bad[4] = o8[6]
+    assert f(ins, o16, bad, 1024, "fp8", "f32", n, stream=0) == mrr.MRR_EOVERLAP
