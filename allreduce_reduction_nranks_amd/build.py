@@ -40,6 +40,12 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+    # Surface compiler warnings; the host pass's note that it does not know
+    # the GPU-only packed-fp32 feature is expected and dropped.
+    warnings = [l for l in r.stderr.splitlines()
+                if "warning:" in l and "packed-fp32-ops" not in l]
+    if warnings:
+        print("\n".join(warnings), file=sys.stderr)
     return obj
 
 

@@ -11,15 +11,18 @@
 // HBM-bound (N*S bytes read, N*S written, ~N VALU adds per element); what
 // decides the bandwidth is how many bytes are in flight and how the 2N
 // same-offset streams hit the DRAM banks:
-//   - the reduce-scatter partition is kept at tile granularity: tile i of
-//     the launch is tile (i % tiles_per_chunk) of chunk
-//     first_chunk + i / tiles_per_chunk, and no tile straddles two chunks;
+//   - the reduce-scatter partition is kept at tile granularity: chunks are
+//     ceil(count / N) elements rounded up to 256 bytes of input (so every
+//     chunk starts on the cache-line grid), tile i of the launch is tile
+//     (i % tiles_per_chunk) of chunk first_chunk + i / tiles_per_chunk, and
+//     no tile straddles two chunks;
 //   - a persistent grid of single-wave (64-lane) workgroups strides over the
-//     tiles; each lane owns U 16-byte vectors of a tile (lane-contiguous, so
-//     every load/store instruction covers 1 KiB of one buffer), issues all
-//     U*N loads (non-temporal: the data is touched once), accumulates each
-//     vector in rank order 0..N-1, narrows once and stores the result to all
-//     N outputs (the all-gather) with non-temporal 16-byte stores;
+//     tiles; each lane owns U units of a tile, a unit being one 16-byte
+//     output vector and its 4 to 16 input bytes per rank (lane-contiguous, so
+//     every store instruction covers 1 KiB of one buffer), issues the loads
+//     of a rank group together (non-temporal: the data is touched once),
+//     accumulates in rank order 0..N-1, narrows once and stores the result
+//     to all N outputs (the all-gather) with non-temporal 16-byte stores;
 //   - few waves per CU stream best (one to eight single-wave workgroups per
 //     CU, see the launch-shape table below): more loads in flight thrash DRAM
 //     rows across the 2N same-offset buffers, fewer leave HBM latency
@@ -118,7 +121,8 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
   bool special[UU];
 #pragma unroll
   for (int u = 0; u < UU; ++u) special[u] = false;
-#pragma unroll(N / G <= 2 ? N / G : 1)
+  constexpr int kGroupUnroll = N / G <= 2 ? N / G : 1;
+#pragma unroll kGroupUnroll
   for (int g = 0; g < N; g += G) {
     uint32_t raw[UU][G][D];
 #pragma unroll
@@ -182,15 +186,15 @@ __device__ __forceinline__ void rsag_vec_body(const RsagArgs& a, void* const* ou
     const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
     if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
       reduce_store<N, In, Acc, Out, U, G, Out2>(a, v0, out2);
-    } else {
-#pragma unroll
+    } else {  // the last, partial tile of a chunk: unit by unit
+#pragma nounroll
       for (int u = 0; u < U; ++u) {
         const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
         if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G, Out2>(a, v, out2);
       }
     }
   }
-  // Elements past the last whole vector (count % VW of them, fewer than one
+  // Elements past the last whole unit (count % UE of them, fewer than one
   // wave) go to the last workgroup, one per lane.
   if (a.tail_count != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < a.tail_count)
     reduce_elem<In, Acc, Out, Out2>(a.in, a.out, N, a.tail_begin + threadIdx.x, out2);
