@@ -241,7 +241,7 @@ def bench_rsag(args, torch, mrr, synth):
     else:
         wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
     sep_us = None
-    if args.layout == "pitch":
+    if args.layout == "pitch" and args.layout_compare:
         def step_sep():
             st = mrr.mrr_allreduce_rsag_ex(ins_sep, outs_sep, count, t, acc, tout, n, rank) \
                 if compiled else mrr.mrr_allreduce(ins_sep, outs_sep, count, t, acc, n)
@@ -505,6 +505,10 @@ def main():
                     help="elements per rank the CPU oracle baseline reduces")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-copy-ceiling", dest="copy_ceiling", action="store_false")
+    ap.add_argument("--layout-compare", action="store_true",
+                    help="also time the same call on one allocation per rank buffer (off by "
+                         "default, so a profiler of the default run sees only the timed "
+                         "configuration's launches)")
     ap.add_argument("--rank", type=int, default=-1,
                     help="RS/AG configs: time only this rank's share (chunk `rank`), -1 = all")
     ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
