@@ -268,3 +268,19 @@ def test_rsag_dual_checks(lib):
     bad = list(o8)
     bad[4] = o8[6]
     assert f(ins, o16, bad, 1024, "fp8", "f32", n, stream=0) == mrr.MRR_EOVERLAP
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "c99"), ("g++", "c++11")])
+def test_header_is_plain_c_and_cxx(tmp_path, compiler, std):
+    """include/mrr.h compiles on its own as C99 and as C++11 with every
+    warning an error: no HIP or torch types leak into the C ABI."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip("%s not present" % compiler)
+    src = tmp_path / ("use.c" if compiler == "gcc" else "use.cpp")
+    src.write_text('#include "mrr.h"\nint f(void) { return (int)MRR_OK + mrr_version(); }\n')
+    r = subprocess.run([compiler, "-std=" + std, "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.dirname(HEADER), "-c", str(src), "-o", str(tmp_path / "u.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
