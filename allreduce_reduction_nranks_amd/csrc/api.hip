@@ -195,15 +195,20 @@ mrr_status mrr_allreduce_rsag(const void* const* inputs, void* const* outputs, s
                                stream);
 }
 
+// The packet entry points refuse counts above this many bytes per rank, and
+// the size helpers return 0 for them (so the products below cannot wrap).
+static bool packet_count_ok(size_t count, int e) { return count <= (SIZE_MAX / 64) / (size_t)e; }
+
 size_t mrr_packet_scratch_bytes(size_t count, mrr_dtype dtype, int nranks) {
   const int e = tsize((int)dtype);
-  if (!e || nranks <= 0) return 0;
+  if (!e || nranks <= 0 || nranks > MRR_MAX_RANKS || !packet_count_ok(count, e)) return 0;
   const size_t npkt = (count * (size_t)e + 3) / 4;
   return (size_t)nranks * (size_t)nranks * npkt * 8;
 }
 
 size_t mrr_packet_flag_bytes(int nranks) {
-  return nranks <= 0 ? 0 : (size_t)nranks * MRR_PKT_FLAG_SLOTS * sizeof(uint32_t);
+  return (nranks <= 0 || nranks > MRR_MAX_RANKS) ? 0
+                                                 : (size_t)nranks * MRR_PKT_FLAG_SLOTS * sizeof(uint32_t);
 }
 
 // Argument checks shared by the packet allreduce entry points; everything
@@ -224,7 +229,7 @@ static mrr_status packet_checks(const char* fn, const void* const* inputs, void*
   if (!aligned(scratch, 8) || !aligned(flags, 4)) return refuse(MRR_EALIGN, fn, "scratch/flags");
   if (count == 0) return MRR_OK;
   const size_t e = tsize(t);
-  if (count > (SIZE_MAX / 64) / e) return refuse(MRR_EINVAL, fn, "count too large");
+  if (!packet_count_ok(count, e)) return refuse(MRR_EINVAL, fn, "count too large");
   for (int r = 0; r < nranks; ++r) {
     if (!inputs[r] || !outputs[r]) return refuse(MRR_EINVAL, fn, "null buffer");
     if (!aligned(inputs[r], 4) || !aligned(outputs[r], 4))
@@ -311,7 +316,7 @@ static uint64_t rsag_chunk_words(size_t count, int e, int nranks) {
 
 size_t mrr_packet_rsag_scratch_bytes(size_t count, mrr_dtype dtype, int nranks) {
   const int e = tsize((int)dtype);
-  if (!e || nranks <= 0) return 0;
+  if (!e || nranks <= 0 || nranks > MRR_MAX_RANKS || !packet_count_ok(count, e)) return 0;
   return 2 * (size_t)nranks * (size_t)nranks * rsag_chunk_words(count, e, nranks) * 8;
 }
 

@@ -207,6 +207,8 @@ mrr_status mrr_allreduce_rsag_dual(const void* const* inputs, void* const* outpu
  * Calls that overlap in time on the same scratch or flags race; calls on one
  * stream never overlap.
  * ------------------------------------------------------------------------ */
+/* Scratch and flag sizes for the calls above; 0 for an unknown type, nranks
+ * outside [1, 32], or a count the entry points refuse as too large. */
 size_t mrr_packet_scratch_bytes(size_t count, mrr_dtype dtype, int nranks);
 size_t mrr_packet_flag_bytes(int nranks);
 
@@ -242,6 +244,7 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
  *   once before first use.
  * Other arguments and errors as mrr_allreduce_packet_ex.
  * ------------------------------------------------------------------------ */
+/* 0 for an unknown type, nranks outside [1, 32], or a count refused as too large. */
 size_t mrr_packet_rsag_scratch_bytes(size_t count, mrr_dtype dtype, int nranks);
 
 mrr_status mrr_allreduce_packet_rsag(const void* const* inputs, void* const* outputs,

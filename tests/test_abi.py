@@ -284,3 +284,13 @@ def test_header_is_plain_c_and_cxx(tmp_path, compiler, std):
                         "-I", os.path.dirname(HEADER), "-c", str(src), "-o", str(tmp_path / "u.o")],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_packet_size_helpers_refuse_what_the_calls_refuse(lib):
+    huge = (1 << 64) - 1
+    for f in (mrr.mrr_packet_scratch_bytes, mrr.mrr_packet_rsag_scratch_bytes):
+        assert f(huge, "f16", 8) == 0
+        assert f(1 << 60, "f32", 8) == 0
+        assert f(1024, "f16", 33) == 0 and f(1024, "f16", 0) == 0
+        assert f(1024, "f16", 8) > 0
+    assert mrr.mrr_packet_flag_bytes(33) == 0 and mrr.mrr_packet_flag_bytes(32) == 32 * 1024 * 4
