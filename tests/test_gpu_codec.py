@@ -1,6 +1,8 @@
 """GPU parity of the standalone FP8 E4M3B15 codec kernels against the CPU
-oracle: every code, every f16 input, and f32 midpoints, neighbours and random
-bit patterns -- bit-exact."""
+oracle: every code, every f16 input and every f32 bit pattern -- bit-exact."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -49,6 +51,36 @@ def test_encode_f32_structured_and_random():
                         np.array([0, -0.0, np.inf, -np.inf, np.nan, 1e-45, 2.0 ** -14], np.float32)])
     out = gpu(mrr.mrr_f32_to_fp8b15, x, torch.uint8, x.size)
     assert_bits_equal(bits(out), oracle.convert(x, "f32", "fp8"), "fp8", "f32->fp8")
+
+
+def test_encode_every_f32_bit_pattern():
+    """All 2^32 f32 inputs (finite, subnormal, infinite and NaN patterns of
+    both signs) through the f32 -> E4M3B15 kernel, in 16 launches of 2^28
+    elements, each against the oracle computed on host threads."""
+    m, sub = 1 << 28, 1 << 24
+    iota = torch.arange(m, dtype=torch.int32, device="cuda")
+    out = torch.empty(m, dtype=torch.uint8, device="cuda")
+    workers = min(16, os.cpu_count() or 1)
+
+    def oracle_slice(lo):  # lo: unsigned bit pattern of the first input
+        u = np.arange(lo, lo + sub, dtype=np.uint64).astype(np.uint32)
+        return oracle.convert(u.view(np.float32), "f32", "fp8")
+
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for s in range(16):
+            base = s * m - (1 << 31)  # signed first pattern; base + m - 1 fits int32
+            announce("codec f32 every pattern", s)
+            x = iota + base
+            assert mrr.mrr_f32_to_fp8b15(x.view(torch.float32), out, m) == mrr.MRR_OK
+            lo = base & 0xFFFFFFFF
+            want = list(pool.map(oracle_slice, range(lo, lo + m, sub)))
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            for j, w in enumerate(want):  # exact codes, NaN codes included
+                g = got[j * sub:(j + 1) * sub]
+                bad = np.flatnonzero(g != w)
+                assert bad.size == 0, "pattern %08x: got %02x want %02x (%d mismatches)" % (
+                    lo + j * sub + bad[0], g[bad[0]], w[bad[0]], bad.size)
 
 
 @pytest.mark.parametrize("off", [1, 3])

@@ -57,6 +57,8 @@ MUTANTS = [
      "rs[((size_t)d * nranks + c) * cw + k] ="),
     ("two-phase all-gather of the input", "make_packet(word_at((const uint8_t*)outputs[0], nbytes, w), flag);",
      "make_packet(word_at((const uint8_t*)inputs[c], nbytes, w), flag);"),
+    ("fp8 encode rounds twice, through f16", "case ORC_FP8: b[0] = narrow_fp8(v); break;",
+     "case ORC_FP8: b[0] = narrow_fp8(f16_value(narrow_f16(v))); break;"),
 ]
 
 
@@ -68,6 +70,7 @@ def _checks():
         pins.test_fp8_worked_values,
         pins.test_fp8_encode_ties_and_saturation,
         pins.test_fp8_encode_all_f16_inputs_brute_force,
+        pins.test_fp8_encode_f32_midpoints_and_random,
         pins.test_f16_decode_all_codes,
         pins.test_bf16_decode_all_codes,
         pins.test_f16_narrow_from_f64_vs_numpy,

@@ -628,3 +628,63 @@ def test_fp8fn_native_accumulation_and_accuracy(orc):
     e32 = np.abs(orc.widen_f64(orc.allreduce(xs, "fp8fn", "f32", "fp8fn"), "fp8fn") - exact)
     e8 = np.abs(FN_VALUES[acc] - exact)
     assert np.all(e32 <= e8)
+
+
+# ---------------------------------------------------------------------------
+# f32 -> FP8 over every f32 bit pattern
+# ---------------------------------------------------------------------------
+
+def f32_encode_steps(mags, nan_code):
+    """The correct f32 -> FP8 encoder on the non-negative half of the bit
+    patterns, as a step function of the pattern u (patterns of one sign are
+    ordered like their values): code j on [starts[j], starts[j+1]).
+
+    The step from code i to i+1 sits at the midpoint of the two magnitudes;
+    the midpoint itself belongs to whichever of the two codes is even.  The
+    largest code runs on through +inf (saturation), then the NaN patterns."""
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    assert np.all(mids.astype(np.float64) == (mags[:-1] + mags[1:]) / 2)  # exact in f32
+    mb = mids.view(np.uint32).astype(np.int64)
+    code_above = np.arange(1, len(mags))
+    starts = np.concatenate([[0], np.where(code_above % 2 == 0, mb, mb + 1), [0x7F800001]])
+    codes = np.concatenate([np.arange(len(mags)), [nan_code]]).astype(np.uint8)
+    assert np.all(np.diff(starts) > 0)
+    return starts, codes
+
+
+def step_values(starts, codes, lo, hi):
+    out = np.empty(hi - lo, np.uint8)
+    j = int(np.searchsorted(starts, lo, side="right")) - 1
+    pos = lo
+    while pos < hi:
+        end = min(hi, int(starts[j + 1])) if j + 1 < len(starts) else hi
+        out[pos - lo:end - lo] = codes[j]
+        pos, j = end, j + 1
+    return out
+
+
+@pytest.mark.parametrize("t", ["fp8", "fp8fn"])
+def test_f32_encode_every_bit_pattern(orc, t):
+    """All 2^32 f32 inputs of the oracle's single-rounding f32 -> FP8 encoder
+    against the step function above, built from magnitudes decoded by
+    library routines (numpy's f16 for E4M3B15, torch's float8_e4m3fn for
+    E4M3FN); negative patterns must give the same code with the sign bit."""
+    from concurrent.futures import ThreadPoolExecutor
+    mags = FP8_MAGS if t == "fp8" else FN_MAGS
+    starts, codes = f32_encode_steps(mags, 0x7F)
+    chunk = 1 << 24
+
+    def run(job):
+        sign, lo = job
+        u = np.arange(lo, lo + chunk, dtype=np.uint32) | np.uint32(sign << 31)
+        got = orc.convert(u.view(np.float32), "f32", t)
+        want = step_values(starts, codes, lo, lo + chunk) | np.uint8(sign << 7)
+        if np.array_equal(got, want):
+            return None
+        i = int(np.flatnonzero(got != want)[0])
+        return "pattern %08x: %02x, want %02x" % (int(u[i]), int(got[i]), int(want[i]))
+
+    jobs = [(s, lo) for s in (0, 1) for lo in range(0, 1 << 31, chunk)]
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as pool:
+        bad = [r for r in pool.map(run, jobs) if r]
+    assert not bad, bad[:4]
