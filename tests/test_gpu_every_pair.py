@@ -6,7 +6,11 @@ accumulation every pair is covered; with native accumulation a quarter of
 them (x_0 among the smallest and the largest patterns of both signs).
 
 Pair i of the 2^32 is x_0 = i >> 16, x_1 = i & 0xFFFF; each launch covers
-2^28 consecutive pairs (4096 values of x_0 against all 65,536 of x_1)."""
+2^28 consecutive pairs (4096 values of x_0 against all 65,536 of x_1).
+
+FP8 inputs (both formats, every code including inf and NaN codes) are
+covered the same way: every pair at two ranks for each accumulator and
+output type, and every triple at three ranks."""
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -61,3 +65,47 @@ def test_n2_every_pair(t, acc, slices):
                 k = s * SLICE + j * SUB
                 assert_bits_equal(got[j * SUB:(j + 1) * SUB], w, t,
                                   "pairs from x0=%04x x1=%04x" % (k >> 16, k & 0xFFFF))
+
+
+FP8_TRIPLES = [(t, a, o) for t in ("fp8", "fp8fn") for a in ("f32", "f16", t) for o in (t, "f16", "f32")]
+
+
+@pytest.mark.parametrize("t,acc,tout", FP8_TRIPLES, ids=["-".join(x) for x in FP8_TRIPLES])
+def test_fp8_n2_every_pair_of_codes(t, acc, tout):
+    """All 65,536 pairs of FP8 codes (inf and NaN codes included) through the
+    two-rank kernel, for every accumulator and output type."""
+    announce("fp8 every pair", t, acc, tout)
+    i = np.arange(65536, dtype=np.uint32)
+    x = [(i >> 8).astype(np.uint8), (i & 0xFF).astype(np.uint8)]
+    ins = [torch.from_numpy(v).cuda() for v in x]
+    outs = [torch.empty(65536, dtype=TORCH[tout], device="cuda") for _ in range(2)]
+    st = mrr.mrr_allreduce_rsag_ex(ins, outs, 65536, t, acc, tout, 2)
+    assert st == mrr.MRR_OK, mrr.mrr_status_string(st)
+    torch.cuda.synchronize()
+    want = oracle.allreduce(x, t, acc, tout)
+    for k in range(2):
+        got = outs[k].cpu().numpy()
+        assert_bits_equal(got.view(want.dtype), want, tout, "out[%d]" % k)
+
+
+@pytest.mark.parametrize("t", ["fp8", "fp8fn"])
+@pytest.mark.parametrize("acc", ["f32", "f16", "native"])
+def test_fp8_n3_every_triple_of_codes(t, acc):
+    """All 2^24 triples of FP8 codes at three ranks, a rank count with no
+    compiled kernel (the size-based dispatcher runs the runtime-N kernel);
+    native accumulation rounds to FP8 after each of the two adds."""
+    acc = t if acc == "native" else acc
+    announce("fp8 every triple", t, acc)
+    i = np.arange(1 << 24, dtype=np.uint32)
+    x = [(i >> 16).astype(np.uint8), ((i >> 8) & 0xFF).astype(np.uint8), (i & 0xFF).astype(np.uint8)]
+    ins = [torch.from_numpy(v).cuda() for v in x]
+    outs = [torch.empty(1 << 24, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    st = mrr.mrr_allreduce(ins, outs, 1 << 24, t, acc, 3)
+    assert st == mrr.MRR_OK, mrr.mrr_status_string(st)
+    sub = 1 << 20
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as pool:
+        want = np.concatenate(list(pool.map(
+            lambda lo: oracle.allreduce([v[lo:lo + sub] for v in x], t, acc, t), range(0, 1 << 24, sub))))
+    torch.cuda.synchronize()
+    for k in range(3):
+        assert_bits_equal(outs[k].cpu().numpy(), want, t, "out[%d]" % k)
