@@ -269,7 +269,28 @@ __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint6
     u32x4 o;
     if constexpr (Out == kFP8) o = special[u] ? encode16<kFP8>(acc[u]) : encode16_fp8_hw(acc[u]);
     else o = encode16<Out>(acc[u]);
-    for (int k = 0; k < n; ++k) st_stream(a.out[k], v, o);
+    if constexpr (G == kAnyGroupWide) {
+      // Above 8 ranks, four output pointers per step: their kernel-argument
+      // loads are issued together and waited for once, instead of one
+      // dependent load per store.  Measured on MI355X, 64 MiB per rank:
+      // 12 ranks 295 -> 283 us, 20 ranks 509 -> 489 us.  At 5 to 8 ranks the
+      // same batching was 2-3 % slower at some counts, so the narrow-group
+      // kernels keep the plain loop.
+      int k = 0;
+      for (; k + 4 <= n; k += 4) {
+        void* const p0 = a.out[k];
+        void* const p1 = a.out[k + 1];
+        void* const p2 = a.out[k + 2];
+        void* const p3 = a.out[k + 3];
+        st_stream(p0, v, o);
+        st_stream(p1, v, o);
+        st_stream(p2, v, o);
+        st_stream(p3, v, o);
+      }
+      for (; k < n; ++k) st_stream(a.out[k], v, o);
+    } else {
+      for (int k = 0; k < n; ++k) st_stream(a.out[k], v, o);
+    }
   }
 }
 
