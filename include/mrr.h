@@ -82,11 +82,12 @@ typedef enum mrr_dtype {
 } mrr_dtype;
 
 /* Packet / RS-AG crossover for mrr_allreduce, measured on one MI355X: 0.
- * There RS/AG is faster at every size (8 ranks of f16: 10.7 us against
- * 12.2-12.7 us up to 64 KiB per rank, 11.2 us against 51.5 us at 1 MiB),
- * because within one GPU it needs no cross-rank synchronisation while
- * packets double the bytes moved.  The pages' selectors, spanning GPUs,
- * switch to RS/AG above 512 KiB (Python default) or 2 MiB (NCCL shim). */
+ * There RS/AG is faster at every size (8 ranks of f16, per call under HIP
+ * graph replay: 2.4 us against 7.6-10.0 us for allpair packets at 16-64 KiB
+ * per rank, 3.7 us against 51.7 us at 1 MiB), because within one GPU it
+ * needs no cross-rank synchronisation while packets double the bytes moved.
+ * The pages' selectors, spanning GPUs, switch to RS/AG above 512 KiB
+ * (Python default) or 2 MiB (NCCL shim). */
 #define MRR_PACKET_MAX_BYTES_ONE_GPU 0
 
 /* Largest rank count any entry point accepts. */
