@@ -688,3 +688,47 @@ def test_f32_encode_every_bit_pattern(orc, t):
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as pool:
         bad = [r for r in pool.map(run, jobs) if r]
     assert not bad, bad[:4]
+
+
+# ---------------------------------------------------------------------------
+# Two ranks, every pair of 16-bit inputs
+# ---------------------------------------------------------------------------
+
+def library_pair_sum(t, x0, x1):
+    """RNE_t(x0 + x1) from library arithmetic: numpy's binary16 add, or
+    torch's float32 add then bfloat16 cast (one f32 rounding before the
+    16-bit one is innocuous: 24 >= 2 * 11 + 2 and 24 >= 2 * 8 + 2)."""
+    if t == "f16":
+        with np.errstate(invalid="ignore", over="ignore"):  # inf - inf, overflow
+            return (np_f16(x0) + np_f16(x1)).view(np.uint16)
+    a = torch.from_numpy(x0.view(np.int16)).view(torch.bfloat16).float()
+    b = torch.from_numpy(x1.view(np.int16)).view(torch.bfloat16).float()
+    return (a + b).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("t", ["f16", "bf16"])
+def test_two_rank_every_pair(orc, t):
+    """All 2^32 pairs (x0, x1) of f16 or bf16 bit patterns -- zeros of both
+    signs, subnormals, infinities, NaNs, overflow -- through the oracle's
+    two-rank reduction with f32 accumulation, against library arithmetic;
+    NaN results need only be NaN on both sides."""
+    from concurrent.futures import ThreadPoolExecutor
+    nan_lo = 0x7C00 if t == "f16" else 0x7F80
+    chunk = 1 << 24
+
+    def run(lo):
+        i = np.arange(lo, lo + chunk, dtype=np.uint64)
+        x0 = (i >> np.uint64(16)).astype(np.uint16)
+        x1 = (i & np.uint64(0xFFFF)).astype(np.uint16)
+        got = orc.allreduce([x0, x1], t, "f32")
+        want = library_pair_sum(t, x0, x1)
+        nan_g, nan_w = (got & 0x7FFF) > nan_lo, (want & 0x7FFF) > nan_lo
+        bad = np.flatnonzero((nan_g != nan_w) | ((got != want) & ~nan_w))
+        if bad.size == 0:
+            return None
+        k = bad[0]
+        return "x0=%04x x1=%04x: %04x, want %04x" % (x0[k], x1[k], got[k], want[k])
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as pool:
+        bad = [r for r in pool.map(run, range(0, 1 << 32, chunk)) if r]
+    assert not bad, bad[:4]
