@@ -85,6 +85,28 @@ int device_cu_count(int device) {
   return cached[device];
 }
 
+// LDS bytes per CU and the most one workgroup may allocate, of the current
+// device (0 when unknown).
+void device_lds_limits(size_t* per_cu, size_t* per_block) {
+  static std::mutex mu;
+  static size_t cached_cu[64] = {0}, cached_block[64] = {0};
+  *per_cu = *per_block = 0;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= 64) return;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached_cu[device] == 0) {
+    int cu = 0, blk = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, device) != hipSuccess)
+      return;
+    cached_cu[device] = cu > 0 ? (size_t)cu : 0;
+    cached_block[device] = blk > 0 ? (size_t)blk : 0;
+  }
+  *per_cu = cached_cu[device];
+  *per_block = cached_block[device];
+}
+
 // Workgroups of `kernel` at `threads` threads that fit on the device at once.
 static int max_resident_blocks(const void* kernel, int threads) {
   int dev = 0;

@@ -131,5 +131,6 @@ hipError_t launch_codec(int dir, const void* in, void* out, size_t n, bool vecto
 
 // ---- device properties ---------------------------------------------------------
 int device_cu_count(int device);
+void device_lds_limits(size_t* per_cu, size_t* per_block);
 
 }  // namespace mrr

@@ -16,17 +16,24 @@
 //     chunk starts on the cache-line grid), tile i of the launch is tile
 //     (i % tiles_per_chunk) of chunk first_chunk + i / tiles_per_chunk, and
 //     no tile straddles two chunks;
-//   - a persistent grid of single-wave (64-lane) workgroups strides over the
-//     tiles; each lane owns U units of a tile, a unit being one 16-byte
-//     output vector and its 4 to 16 input bytes per rank (lane-contiguous, so
-//     every store instruction covers 1 KiB of one buffer), issues the loads
-//     of a rank group together (non-temporal: the data is touched once),
+//   - one single-wave (64-lane) workgroup per tile, so the hardware
+//     dispatcher hands tiles out in launch order as workgroups retire and the
+//     2N active address windows stay as narrow as the resident workgroups;
+//     each lane owns U units of a tile, a unit being one 16-byte output
+//     vector and its 4 to 16 input bytes per rank (lane-contiguous, so every
+//     store instruction covers 1 KiB of one buffer), issues the loads of a
+//     rank group together (non-temporal: the data is touched once),
 //     accumulates in rank order 0..N-1, narrows once and stores the result
 //     to all N outputs (the all-gather) with non-temporal 16-byte stores;
-//   - few waves per CU stream best (one to eight single-wave workgroups per
-//     CU, see the launch-shape table below): more loads in flight thrash DRAM
-//     rows across the 2N same-offset buffers, fewer leave HBM latency
-//     exposed.
+//   - few waves per CU stream best (four to twelve single-wave workgroups
+//     per CU, see the launch-shape table below): more loads in flight thrash
+//     DRAM rows across the 2N same-offset buffers, fewer leave HBM latency
+//     exposed.  The cap is enforced by giving each workgroup an LDS
+//     reservation of 1/cap of the CU's LDS, which the kernels never touch.
+//   - A persistent grid that strides over the tiles was measured slower on
+//     MI355X, increasingly so the more tiles each workgroup walks (8 x 256 MiB
+//     bf16: 0.69 of the HBM peak against 0.77; 2 x 2 GiB: 0.66 against 0.74):
+//     workgroups drift apart over a long launch and the active windows widen.
 // No __restrict__: an output may be its own rank's input (in place); a lane
 // reads every element it writes before writing it.
 #include <stdlib.h>
@@ -38,35 +45,41 @@ namespace mrr {
 
 constexpr int kRsagThreads = 64;  // one wave per workgroup
 
-// Launch shape, from a sweep of (units per lane U) x (workgroups per CU)
-// of this kernel on MI355X (64 MiB and 256 MiB per rank).  Streaming
-// bandwidth is bumpy in both knobs -- the 2N same-offset streams interact
-// with the DRAM channel and bank mapping -- so each entry is the setting that
-// stayed near the best across buffer sizes rather than a formula.
-//   16-bit and 32-bit inputs: N=2 U=8 x2, N=4 U=4 x4, N=8 U=1 x6,
-//                             N=16 U=1 x3, N=32 U=1 x8 (workgroups per CU;
-//                             N=16 from interleaved runs at 64 and 256 MiB,
-//                             +1.5 % over U=2 x2; at N=32 four per CU is 1 %
-//                             faster at 64 MiB but 19 % slower at 256 MiB)
-//   FP8 inputs (E4M3B15 and OCP E4M3FN): N=2: U=4 times 2 for f16 and 4 for
-//                             f32 outputs (a lane loads 16 bytes per rank),
-//                             4 workgroups per CU (3 for f16 out); N>2:
-//                             FP8 out U=1 x4 (E4M3FN out x6: its shorter
-//                             body needs more waves in flight), f16 out U=2
-//                             x3, f32 out U=1 x8 (a lane loads 4 bytes per
-//                             rank; 8 x 32 MiB E4M3B15 264.7 us against
-//                             265.9 us at U=4 x4).
+// Launch shape, from sweeps of (units per lane U) x (workgroups per CU) of
+// this kernel on MI355X at 64 MiB and 256 MiB per rank (16- and 32-bit
+// inputs) and 32 MiB per rank (FP8 inputs at 8 ranks).  Streaming bandwidth is
+// bumpy in both knobs -- the 2N same-offset streams interact with the DRAM
+// channel and bank mapping -- so each entry is the setting that stayed near
+// the best across buffer sizes rather than a formula.
+//   16-bit and 32-bit inputs: N=2 U=2 x12, N=4 U=1 x8, N=8 U=1 x8,
+//                             N=16 U=1 x4, N=32 U=1 x8 (fractions of the HBM
+//                             peak at 64 / 256 MiB per rank: N=2 0.81 / 0.82,
+//                             N=4 0.82 / 0.80, N=8 0.81 (f16) / 0.77,
+//                             N=16 0.78 / 0.76, N=32 - / 0.71)
+//   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: FP8 out U=1 x8 (E4M3FN out x6),
+//                             f16 out U=1 x6, f32 out U=2 x6 (E4M3FN x4: its
+//                             cheaper decode wants fewer waves);
+//                             N=2: U=4 times 2 for f16 and 4 for f32 outputs
+//                             (a lane loads 16 bytes per rank), 4 workgroups
+//                             per CU (3 for f16 out, 6 for E4M3FN out).
+//   One-pass FP8 -> f16 + FP8 (rsag_dual_kernel): U=2 x4 (U=8 x3 at N=2).
 constexpr int rsag_unroll(int n, int tin, int tout) {
   if (is_fp8(tin)) {
     if (n == 2) return 4 * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
-    return tout == kF16 ? 2 : 1;
+    return tout == kF32 ? 2 : 1;
   }
-  return n == 2 ? 8 : n == 4 ? 4 : 1;
+  return n == 2 ? 2 : 1;
 }
 constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
-  if (is_fp8(tin)) return tout == kF16 ? 3 : tout == kFP8FN ? 6 : (tout == kF32 && n > 2) ? 8 : 4;
-  return n == 2 ? 2 : n == 4 ? 4 : n == 8 ? 6 : n == 16 ? 3 : 8;
+  if (is_fp8(tin)) {
+    if (n == 2) return tout == kF16 ? 3 : tout == kFP8FN ? 6 : 4;
+    if (tout == kF32) return tin == kFP8FN ? 4 : 6;
+    return tout == kFP8 ? 8 : 6;
+  }
+  return n == 2 ? 12 : n == 4 ? 8 : n == 8 ? 8 : n == 16 ? 4 : 8;
 }
+constexpr int rsag_dual_unroll(int n) { return n == 2 ? 8 : 2; }
+constexpr int rsag_dual_wg_per_cu(int n) { return n == 2 ? 3 : 4; }
 // Ranks whose vectors are loaded together before they are added: all of them
 // up to 16 ranks; groups of 16 above that, and groups of 8 for FP8 inputs or
 // an FP8 accumulator (16 values per vector and two decode paths make the
@@ -351,14 +364,43 @@ bool rsag_supported(int nranks, int tin, int tacc, int tout) {
   return valid_nranks(nranks) && rsag_types_supported(tin, tacc, tout);
 }
 
+// Launch shape: one workgroup per tile (at most kMaxGrid; past that each
+// workgroup walks several tiles) and a dynamic LDS reservation that lets at
+// most `wpc` workgroups share a CU (MRR_RSAG_WPC overrides the table).  The
+// reservation is the CU's LDS divided by wpc, rounded down to 1 KiB, so that
+// wpc of them fit and one more does not; it is clamped to what a workgroup
+// may allocate, and left at 0 (no cap) where the device reports no LDS size.
+struct RsagShape {
+  dim3 grid;
+  size_t lds;
+};
+constexpr uint32_t kMaxGrid = 1u << 24;
+
+static RsagShape rsag_shape(int wpc, uint32_t launch_tiles) {
+  static const int wpc_env = [] {
+    const char* v = getenv("MRR_RSAG_WPC");
+    return v ? atoi(v) : 0;
+  }();
+  if (wpc_env > 0) wpc = wpc_env;
+  RsagShape sh;
+  const uint32_t blocks = launch_tiles < kMaxGrid ? launch_tiles : kMaxGrid;
+  sh.grid = dim3(blocks ? blocks : 1);  // at least one: a tail-only launch
+  size_t per_cu = 0, per_block = 0;
+  device_lds_limits(&per_cu, &per_block);
+  size_t lds = wpc > 0 ? per_cu / (size_t)wpc / 1024 * 1024 : 0;
+  if (lds > per_block) lds = per_block;
+  sh.lds = lds;
+  return sh;
+}
+
 template <int In, int Acc, int Out>
-static void launch_vec_typed(int nranks, dim3 grid, const RsagArgs& a, hipStream_t s) {
+static void launch_vec_typed(int nranks, const RsagShape& sh, const RsagArgs& a, hipStream_t s) {
   const dim3 block(kRsagThreads);
   switch (nranks) {
 #define MRR_CASE(N)                                                                        \
   case N:                                                                                  \
-    hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In, Out)>), grid, block, \
-                       0, s, a);                                                           \
+    hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In, Out)>), sh.grid, block, \
+                       sh.lds, s, a);                                                      \
     break;
     MRR_CASE(2) MRR_CASE(4) MRR_CASE(8) MRR_CASE(16) MRR_CASE(32)
 #undef MRR_CASE
@@ -369,9 +411,11 @@ static void launch_vec_typed(int nranks, dim3 grid, const RsagArgs& a, hipStream
 // The runtime-N kernel loads 16 bytes per lane per rank like the compiled
 // ones at N = 8, times a multiplier M of units per lane for 16- and 32-bit
 // inputs so that small rank counts still keep enough loads in flight.
-// Measured on MI355X (64-128 MiB per rank; M in {1,2,4} x 2-8 workgroups per
-// CU): N <= 4: M=4, 8 per CU; N <= 8: M=2, 4 per CU; N <= 16: M=1, 4 per CU;
-// N > 16: M=1, 2 per CU.  FP8 inputs keep M=1 and 6 per CU.
+// Measured on MI355X (64-128 MiB per rank): M=4 for N <= 4, M=2 for N <= 8,
+// M=1 above; workgroups per CU (one per tile, capped as for the compiled
+// kernels, 4-16 swept at 64 MiB per rank): 12 for N <= 4, 4 above
+// (3 x f16 0.76 of the HBM peak, 6 x bf16 0.77, 12 x f16 0.78,
+// 24 x bf16 0.73).  FP8 inputs keep M=1 and 6 per CU.
 // MRR_RSAG_ANY_M and MRR_RSAG_WPC override.
 constexpr int rsag_any_unroll(int tin, int tout) {
   return is_fp8(tin) ? (tout == kF32 ? 4 : tout == kF16 ? 2 : 1) : 1;
@@ -379,11 +423,14 @@ constexpr int rsag_any_unroll(int tin, int tout) {
 static int rsag_any_multiplier(int n) { return n <= 4 ? 4 : n <= 8 ? 2 : 1; }
 static int rsag_any_wg_per_cu(int n, int tin) {
   if (is_fp8(tin)) return 6;
-  return n <= 4 ? 8 : n <= 16 ? 4 : 2;
+  return n <= 4 ? 12 : 4;
 }
 
 template <int In, int Acc, int Out>
-static void launch_any_typed(int n, int mult, dim3 grid, const RsagArgs& a, hipStream_t s) {
+static void launch_any_typed(int n, int mult, const RsagShape& sh, const RsagArgs& a,
+                             hipStream_t s) {
+  const dim3 grid = sh.grid;
+  const size_t lds = sh.lds;
   constexpr int U = rsag_any_unroll(In, Out);
   const dim3 block(kRsagThreads);
   // FP8 data or accumulators keep groups of 8 (as the compiled kernels do):
@@ -391,16 +438,16 @@ static void launch_any_typed(int n, int mult, dim3 grid, const RsagArgs& a, hipS
   constexpr bool wide_ok = !is_fp8(In) && !is_fp8(Acc);
   if (wide_ok && n > kAnyGroup) {
     hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, wide_ok ? kAnyGroupWide : kAnyGroup>), grid,
-                       block, 0, s, a);
+                       block, lds, s, a);
   } else if constexpr (is_fp8(In)) {
-    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, lds, s, a);
   } else {
     if (mult == 4)
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 4 * U, kAnyGroup>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 4 * U, kAnyGroup>), grid, block, lds, s, a);
     else if (mult == 2)
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 2 * U, kAnyGroup>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 2 * U, kAnyGroup>), grid, block, lds, s, a);
     else
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, lds, s, a);
   }
 }
 
@@ -441,21 +488,6 @@ static void rsag_geometry(const RsagPlan& p, uint64_t vw, uint64_t ue, uint64_t 
     a.tail_count = tail_chunk == (uint64_t)p.rank ? tail : 0;
     a.launch_tiles = a.tiles_per_chunk;
   }
-}
-
-// Persistent grid: wpc workgroups per CU (MRR_RSAG_WPC overrides), at most
-// one per tile, at least one (a tail-only launch).
-static dim3 rsag_grid(int wpc, uint32_t launch_tiles) {
-  static const int wpc_env = [] {
-    const char* v = getenv("MRR_RSAG_WPC");
-    return v ? atoi(v) : 0;
-  }();
-  if (wpc_env > 0) wpc = wpc_env;
-  uint64_t blocks = (uint64_t)device_cu_count(-1) * (uint64_t)wpc;
-  if (blocks == 0) blocks = 1024;
-  if (blocks > launch_tiles) blocks = launch_tiles;
-  if (blocks == 0) blocks = 1;
-  return dim3((uint32_t)blocks);
 }
 
 template <int In, int Acc, int Out>
@@ -504,12 +536,12 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     if (any_n)
       rsag_geometry(p, vw, ue, (uint64_t)kRsagThreads * rsag_any_unroll(In, Out) * mult, a);
     if (a.launch_tiles == 0 && a.tail_count == 0) return hipSuccess;
-    const dim3 grid = rsag_grid(small ? 8 : any_n ? rsag_any_wg_per_cu(n, In) : rsag_wg_per_cu(n, In, Out),
-                                a.launch_tiles);
+    const RsagShape sh = rsag_shape(
+        small ? 8 : any_n ? rsag_any_wg_per_cu(n, In) : rsag_wg_per_cu(n, In, Out), a.launch_tiles);
     if (any_n)
-      launch_any_typed<In, Acc, Out>(n, mult, grid, a, stream);
+      launch_any_typed<In, Acc, Out>(n, mult, sh, a, stream);
     else
-      launch_vec_typed<In, Acc, Out>(n, grid, a, stream);
+      launch_vec_typed<In, Acc, Out>(n, sh, a, stream);
   } else {
     RsagScalarArgs a = {};
     for (int r = 0; r < n; ++r) {
@@ -569,15 +601,15 @@ static hipError_t launch_rsag_dual_typed(const RsagPlan& p, const void* const* i
   }
   constexpr uint64_t vw = kChunkAlignBytes / Ty<In>::size;
   constexpr uint64_t ue = Unit<In, kF16>::UE;
-  rsag_geometry(p, vw, ue, (uint64_t)kRsagThreads * rsag_unroll(n, In, kF16), d.base);
+  rsag_geometry(p, vw, ue, (uint64_t)kRsagThreads * rsag_dual_unroll(n), d.base);
   if (d.base.launch_tiles == 0 && d.base.tail_count == 0) return hipSuccess;
-  const dim3 grid = rsag_grid(rsag_wg_per_cu(n, In, kF16), d.base.launch_tiles);
+  const RsagShape sh = rsag_shape(rsag_dual_wg_per_cu(n), d.base.launch_tiles);
   const dim3 block(kRsagThreads);
   switch (n) {
 #define MRR_CASE(N)                                                                          \
   case N:                                                                                    \
-    hipLaunchKernelGGL((rsag_dual_kernel<N, In, Acc, rsag_unroll(N, In, kF16)>), grid, block, 0, \
-                       stream, d);                                                           \
+    hipLaunchKernelGGL((rsag_dual_kernel<N, In, Acc, rsag_dual_unroll(N)>), sh.grid, block,    \
+                       sh.lds, stream, d);                                                   \
     break;
     MRR_CASE(2) MRR_CASE(4) MRR_CASE(8) MRR_CASE(16) MRR_CASE(32)
 #undef MRR_CASE
