@@ -107,6 +107,31 @@ void device_lds_limits(size_t* per_cu, size_t* per_block) {
   *per_block = cached_block[device];
 }
 
+// Dynamic LDS bytes that let at most `wpc` workgroups share a CU: the CU's
+// LDS divided by wpc, rounded down to 1 KiB, clamped to what one workgroup may
+// allocate; 0 (no cap) when wpc <= 0 or the device reports no LDS size.  On
+// MI355X (160 KiB per CU) the LDS is handed out in two halves of 80 KiB, so
+// an odd cap behaves as the even cap below it (caps 2 and 3 were measured to
+// time the same); the launch tables use even caps.
+size_t occupancy_lds_bytes(int wpc) {
+  if (wpc <= 0) return 0;
+  size_t per_cu = 0, per_block = 0;
+  device_lds_limits(&per_cu, &per_block);
+  size_t lds = per_cu / (size_t)wpc / 1024 * 1024;
+  if (lds > per_block) lds = per_block;
+  return lds;
+}
+
+// MRR_MAX_GRID=<g> limits the one-workgroup-per-tile launches (RS/AG and
+// codec) to g workgroups, each then walking several tiles; read at every call
+// so that a test can exercise that path at small sizes.  0 when unset.
+uint32_t max_grid_override() {
+  const char* v = getenv("MRR_MAX_GRID");
+  if (!v) return 0;
+  const long g = atol(v);
+  return g > 0 && g < (1L << 30) ? (uint32_t)g : 0;
+}
+
 // Workgroups of `kernel` at `threads` threads that fit on the device at once.
 static int max_resident_blocks(const void* kernel, int threads) {
   int dev = 0;

@@ -11,6 +11,9 @@
 // store instruction of a wave covers one contiguous span (1 KiB on the wide
 // side, 256 or 512 B on the narrow side) and writes whole cache lines.  Each
 // lane keeps U units in flight; the last n % V elements go one by one.
+// One workgroup per tile, dispatched in order, with residency capped by an
+// unused LDS reservation (as for the RS/AG kernels): a persistent grid that
+// strides over the tiles was measured 7-18 % slower on MI355X.
 #include <cstdlib>
 
 #include "mrr_device.hpp"
@@ -108,16 +111,20 @@ __global__ void __launch_bounds__(kCodecThreads) codec_scalar_k(const void* in, 
 }
 
 // Units in flight per lane and 256-lane workgroups per CU, per direction,
-// measured on MI355X over 268,435,456 elements (U in {1,2,4,8} x {4,8,16}
-// workgroups per CU): U=8 and 16 per CU for both decodes and the f16 encode;
-// the f32 encode, whose lanes already load 64 B per unit group, is best at
-// U=4 and 4 per CU.  MRR_CODEC_U / MRR_CODEC_WPC override.
-constexpr int codec_unroll(int dir) { return dir == kEncF32 ? 4 : 8; }
-constexpr int codec_wg_per_cu(int dir) { return dir == kEncF32 ? 4 : 16; }
-
+// measured on MI355X over 268,435,456 elements (U in {1,2,4,8} x {2..8}
+// workgroups per CU, one workgroup per tile): both decodes U=4 at 4 per CU
+// (fractions of the HBM peak: f16 0.79, f32 0.82), the f16 encode U=4 at 6
+// per CU (0.81) and the f32 encode U=2 at 6 per CU (0.81-0.83).
+// MRR_CODEC_U / MRR_CODEC_WPC override.
+constexpr int codec_unroll(int dir) { return dir == kEncF32 ? 2 : 4; }
+constexpr int codec_wg_per_cu(int dir) { return dir == kDecF16 || dir == kDecF32 ? 4 : 6; }
+// At most 2^22 workgroups of 256 lanes (2^30 work-items); past that a workgroup
+// walks several tiles.
+constexpr uint64_t kCodecMaxGrid = 1u << 22;
 template <int Dir, int U>
-static void launch_vec_u(dim3 grid, const void* in, void* out, uint64_t n, hipStream_t s) {
-  hipLaunchKernelGGL((codec_vec_k<Dir, U>), grid, dim3(kCodecThreads), 0, s, in, out, n);
+static void launch_vec_u(dim3 grid, size_t lds, const void* in, void* out, uint64_t n,
+                         hipStream_t s) {
+  hipLaunchKernelGGL((codec_vec_k<Dir, U>), grid, dim3(kCodecThreads), lds, s, in, out, n);
 }
 
 template <int Dir>
@@ -130,8 +137,13 @@ static hipError_t launch_codec_dir(const void* in, void* out, uint64_t n, bool v
   const uint64_t units = n / CodecShape<Dir>::V;
   const uint64_t work = vector ? (units + (uint64_t)kCodecThreads * U - 1) / ((uint64_t)kCodecThreads * U)
                                : (n + kCodecThreads - 1) / kCodecThreads;
+  // Vector path: one workgroup per tile, residency capped through LDS.  The
+  // element-wise path (unaligned pointers) keeps a grid of wpc workgroups
+  // per CU striding over the elements.
   uint64_t blocks = work;
-  uint64_t cap = (uint64_t)device_cu_count(-1) * wpc;
+  const uint64_t g_env = max_grid_override();
+  uint64_t cap = vector ? (g_env > 0 && g_env < kCodecMaxGrid ? g_env : kCodecMaxGrid)
+                        : (uint64_t)device_cu_count(-1) * wpc;
   if (cap == 0) cap = 2048;
   if (blocks > cap) blocks = cap;
   if (blocks == 0) blocks = 1;  // tail only
@@ -139,11 +151,12 @@ static hipError_t launch_codec_dir(const void* in, void* out, uint64_t n, bool v
   if (!vector) {
     hipLaunchKernelGGL(codec_scalar_k<Dir>, grid, dim3(kCodecThreads), 0, stream, in, out, n);
   } else {
+    const size_t lds = occupancy_lds_bytes((int)wpc);
     switch (U) {
-      case 1: launch_vec_u<Dir, 1>(grid, in, out, n, stream); break;
-      case 2: launch_vec_u<Dir, 2>(grid, in, out, n, stream); break;
-      case 4: launch_vec_u<Dir, 4>(grid, in, out, n, stream); break;
-      default: launch_vec_u<Dir, 8>(grid, in, out, n, stream); break;
+      case 1: launch_vec_u<Dir, 1>(grid, lds, in, out, n, stream); break;
+      case 2: launch_vec_u<Dir, 2>(grid, lds, in, out, n, stream); break;
+      case 4: launch_vec_u<Dir, 4>(grid, lds, in, out, n, stream); break;
+      default: launch_vec_u<Dir, 8>(grid, lds, in, out, n, stream); break;
     }
   }
   return hipGetLastError();

@@ -132,5 +132,9 @@ hipError_t launch_codec(int dir, const void* in, void* out, size_t n, bool vecto
 // ---- device properties ---------------------------------------------------------
 int device_cu_count(int device);
 void device_lds_limits(size_t* per_cu, size_t* per_block);
+// Dynamic LDS per workgroup that caps residency at `wpc` workgroups per CU.
+size_t occupancy_lds_bytes(int wpc);
+// MRR_MAX_GRID (read at every call), 0 when unset.
+uint32_t max_grid_override();
 
 }  // namespace mrr

@@ -60,9 +60,12 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup
 //                             f16 out U=1 x6, f32 out U=2 x6 (E4M3FN x4: its
 //                             cheaper decode wants fewer waves);
 //                             N=2: U=4 times 2 for f16 and 4 for f32 outputs
-//                             (a lane loads 16 bytes per rank), 4 workgroups
-//                             per CU (3 for f16 out, 6 for E4M3FN out).
-//   One-pass FP8 -> f16 + FP8 (rsag_dual_kernel): U=2 x4 (U=8 x3 at N=2).
+//                             (a lane loads 16 bytes per rank); workgroups per
+//                             CU (2-8 swept at 32 MiB per rank) E4M3B15: 8 for
+//                             FP8 out, 6 for f16, 8 for f32; E4M3FN: 8 for FP8
+//                             out, 4 for f16, 2 for f32.
+//   One-pass FP8 -> f16 + FP8 (rsag_dual_kernel): U=2 x4 (U=8 x4 at N=2; 2-8
+//                             swept at 8 x 32 MiB and 2 x 32 MiB).
 constexpr int rsag_unroll(int n, int tin, int tout) {
   if (is_fp8(tin)) {
     if (n == 2) return 4 * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
@@ -72,14 +75,17 @@ constexpr int rsag_unroll(int n, int tin, int tout) {
 }
 constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
   if (is_fp8(tin)) {
-    if (n == 2) return tout == kF16 ? 3 : tout == kFP8FN ? 6 : 4;
+    if (n == 2) {
+      if (tin == kFP8FN) return tout == kF32 ? 2 : tout == kF16 ? 4 : 8;
+      return tout == kF16 ? 6 : 8;
+    }
     if (tout == kF32) return tin == kFP8FN ? 4 : 6;
     return tout == kFP8 ? 8 : 6;
   }
   return n == 2 ? 12 : n == 4 ? 8 : n == 8 ? 8 : n == 16 ? 4 : 8;
 }
 constexpr int rsag_dual_unroll(int n) { return n == 2 ? 8 : 2; }
-constexpr int rsag_dual_wg_per_cu(int n) { return n == 2 ? 3 : 4; }
+constexpr int rsag_dual_wg_per_cu(int) { return 4; }
 // Ranks whose vectors are loaded together before they are added: all of them
 // up to 16 ranks; groups of 16 above that, and groups of 8 for FP8 inputs or
 // an FP8 accumulator (16 values per vector and two decode paths make the
@@ -366,10 +372,8 @@ bool rsag_supported(int nranks, int tin, int tacc, int tout) {
 
 // Launch shape: one workgroup per tile (at most kMaxGrid; past that each
 // workgroup walks several tiles) and a dynamic LDS reservation that lets at
-// most `wpc` workgroups share a CU (MRR_RSAG_WPC overrides the table).  The
-// reservation is the CU's LDS divided by wpc, rounded down to 1 KiB, so that
-// wpc of them fit and one more does not; it is clamped to what a workgroup
-// may allocate, and left at 0 (no cap) where the device reports no LDS size.
+// most `wpc` workgroups share a CU (occupancy_lds_bytes; MRR_RSAG_WPC
+// overrides the table).
 struct RsagShape {
   dim3 grid;
   size_t lds;
@@ -383,13 +387,11 @@ static RsagShape rsag_shape(int wpc, uint32_t launch_tiles) {
   }();
   if (wpc_env > 0) wpc = wpc_env;
   RsagShape sh;
-  const uint32_t blocks = launch_tiles < kMaxGrid ? launch_tiles : kMaxGrid;
+  const uint32_t g_env = max_grid_override();
+  const uint32_t max_grid = g_env > 0 && g_env < kMaxGrid ? g_env : kMaxGrid;
+  const uint32_t blocks = launch_tiles < max_grid ? launch_tiles : max_grid;
   sh.grid = dim3(blocks ? blocks : 1);  // at least one: a tail-only launch
-  size_t per_cu = 0, per_block = 0;
-  device_lds_limits(&per_cu, &per_block);
-  size_t lds = wpc > 0 ? per_cu / (size_t)wpc / 1024 * 1024 : 0;
-  if (lds > per_block) lds = per_block;
-  sh.lds = lds;
+  sh.lds = occupancy_lds_bytes(wpc);
   return sh;
 }
 

@@ -51,7 +51,7 @@ def test_parity_small(n, t, acc, tout):
 
 
 # Calls whose compiled kernel would have fewer than 2 tiles per CU run the
-# runtime-N kernel instead (N = 2, 4 for 16/32-bit data, N = 2 for FP8), so
+# runtime-N kernel instead (N = 2 for 16/32-bit and FP8 data), so
 # test_parity_small covers that route for them.  These sizes put the same
 # rank counts well above that threshold (3x, on 256 CUs) so the compiled
 # kernels, at the units per lane of their launch table, are covered too.
@@ -60,11 +60,12 @@ OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
 
 
 def table_unroll(n, t, tout):
+    # units per lane of the compiled kernels' launch table (rsag.hip)
     if t in ("fp8", "fp8fn"):
         if n == 2:
             return 4 * {"f32": 4, "f16": 2}.get(tout, 1)
-        return 2 if tout == "f16" else 1
-    return {2: 8, 4: 4}.get(n, 1)
+        return 2 if tout == "f32" else 1
+    return 2 if n == 2 else 1
 
 
 VEC_CASES = [(n, t, a, o) for (t, a, o) in TRIPLES + FN_TRIPLES
@@ -290,3 +291,35 @@ def test_rank_sweep_256mib_bf16_sampled(n):
             assert torch.equal(outs[k].view(torch.int16), outs[0].view(torch.int16))
     del ins, outs
     torch.cuda.empty_cache()
+
+
+# Launches of more tiles than MRR_MAX_GRID workgroups: each workgroup walks
+# several tiles (the path calls above 2^24 tiles take), including partial
+# tiles at chunk ends and the element tail.  The override is read per call.
+WALK_CASES = [(2, "bf16", "f32", "bf16"), (8, "f16", "f32", "f16"), (16, "f32", "f32", "f32"),
+              (32, "bf16", "f32", "bf16"), (8, "fp8", "f32", "fp8"), (8, "fp8fn", "f32", "f32"),
+              (4, "fp8", "f32", "f16")]
+
+
+@pytest.mark.parametrize("n,t,acc,tout", WALK_CASES, ids=["%d-%s-%s-%s" % c for c in WALK_CASES])
+@pytest.mark.parametrize("grid", [1, 7, 300])
+def test_parity_workgroups_walk_tiles(n, t, acc, tout, grid, monkeypatch):
+    count = n * 64 * 2 * (3 * 512 // n + 1) * (16 // OUT_SIZE[tout]) + 13
+    announce("rsag tile walk", n, t, acc, tout, count, "grid", grid)
+    ins = inputs_for(t, n, count, seed0=70 * n + grid)
+    monkeypatch.setenv("MRR_MAX_GRID", str(grid))
+    outs = run(ins, t, acc, tout)
+    for r in (0, n - 1):
+        share = run(ins, t, acc, tout, rank=r, outs=[empty(tout, count, 0x5A) for _ in range(n)])
+        chunk = -(-(-(-count // n)) // CHUNK_ALIGN[t]) * CHUNK_ALIGN[t]
+        lo, hi = min(count, r * chunk), min(count, (r + 1) * chunk)
+        want_share = oracle.allreduce([bits(x)[lo:hi] for x in ins], t, acc, tout)
+        for k, o in enumerate(share):
+            assert_bits_equal(bits(o)[lo:hi], want_share, tout, "rank %d share out[%d]" % (r, k))
+            raw = o.view(torch.uint8).cpu().numpy()
+            esz = OUT_SIZE[tout]
+            assert np.all(raw[:lo * esz] == 0x5A) and np.all(raw[hi * esz:] == 0x5A), \
+                "rank %d share wrote outside its chunk" % r
+    monkeypatch.delenv("MRR_MAX_GRID")
+    want = oracle.allreduce([bits(x) for x in ins], t, acc, tout)
+    check_all(outs, want, tout, "walk n=%d %s/%s/%s grid %d" % (n, t, acc, tout, grid))
