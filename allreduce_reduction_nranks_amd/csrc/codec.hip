@@ -138,12 +138,15 @@ static hipError_t launch_codec_dir(const void* in, void* out, uint64_t n, bool v
   const uint64_t work = vector ? (units + (uint64_t)kCodecThreads * U - 1) / ((uint64_t)kCodecThreads * U)
                                : (n + kCodecThreads - 1) / kCodecThreads;
   // Vector path: one workgroup per tile, residency capped through LDS.  The
-  // element-wise path (unaligned pointers) keeps a grid of wpc workgroups
-  // per CU striding over the elements.
+  // element-wise path (unaligned pointers), and the vector path with
+  // MRR_LDS_CAP=0, keep a grid of wpc workgroups per CU striding over the
+  // work.
   uint64_t blocks = work;
   const uint64_t g_env = max_grid_override();
-  uint64_t cap = vector ? (g_env > 0 && g_env < kCodecMaxGrid ? g_env : kCodecMaxGrid)
+  const bool capped = vector && lds_cap_enabled();
+  uint64_t cap = capped ? (g_env > 0 && g_env < kCodecMaxGrid ? g_env : kCodecMaxGrid)
                         : (uint64_t)device_cu_count(-1) * wpc;
+  if (!capped && g_env > 0 && g_env < cap) cap = g_env;
   if (cap == 0) cap = 2048;
   if (blocks > cap) blocks = cap;
   if (blocks == 0) blocks = 1;  // tail only
@@ -151,7 +154,7 @@ static hipError_t launch_codec_dir(const void* in, void* out, uint64_t n, bool v
   if (!vector) {
     hipLaunchKernelGGL(codec_scalar_k<Dir>, grid, dim3(kCodecThreads), 0, stream, in, out, n);
   } else {
-    const size_t lds = occupancy_lds_bytes((int)wpc);
+    const size_t lds = capped ? occupancy_lds_bytes((int)wpc) : 0;
     switch (U) {
       case 1: launch_vec_u<Dir, 1>(grid, lds, in, out, n, stream); break;
       case 2: launch_vec_u<Dir, 2>(grid, lds, in, out, n, stream); break;

@@ -136,5 +136,7 @@ void device_lds_limits(size_t* per_cu, size_t* per_block);
 size_t occupancy_lds_bytes(int wpc);
 // MRR_MAX_GRID (read at every call), 0 when unset.
 uint32_t max_grid_override();
+// False when MRR_LDS_CAP=0 (read at every call): persistent grids, no LDS reservation.
+bool lds_cap_enabled();
 
 }  // namespace mrr

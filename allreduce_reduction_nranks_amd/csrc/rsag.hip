@@ -373,7 +373,8 @@ bool rsag_supported(int nranks, int tin, int tacc, int tout) {
 // Launch shape: one workgroup per tile (at most kMaxGrid; past that each
 // workgroup walks several tiles) and a dynamic LDS reservation that lets at
 // most `wpc` workgroups share a CU (occupancy_lds_bytes; MRR_RSAG_WPC
-// overrides the table).
+// overrides the table).  With MRR_LDS_CAP=0, a persistent grid of wpc
+// workgroups per CU and no reservation.
 struct RsagShape {
   dim3 grid;
   size_t lds;
@@ -387,11 +388,16 @@ static RsagShape rsag_shape(int wpc, uint32_t launch_tiles) {
   }();
   if (wpc_env > 0) wpc = wpc_env;
   RsagShape sh;
+  const bool capped = lds_cap_enabled();
   const uint32_t g_env = max_grid_override();
-  const uint32_t max_grid = g_env > 0 && g_env < kMaxGrid ? g_env : kMaxGrid;
+  uint32_t max_grid = g_env > 0 && g_env < kMaxGrid ? g_env : kMaxGrid;
+  if (!capped) {  // persistent grid: wpc workgroups per CU stride over the tiles
+    const uint64_t p = (uint64_t)device_cu_count(-1) * (uint64_t)(wpc > 0 ? wpc : 1);
+    if (p > 0 && p < max_grid) max_grid = (uint32_t)p;
+  }
   const uint32_t blocks = launch_tiles < max_grid ? launch_tiles : max_grid;
   sh.grid = dim3(blocks ? blocks : 1);  // at least one: a tail-only launch
-  sh.lds = occupancy_lds_bytes(wpc);
+  sh.lds = capped ? occupancy_lds_bytes(wpc) : 0;
   return sh;
 }
 

@@ -323,3 +323,17 @@ def test_parity_workgroups_walk_tiles(n, t, acc, tout, grid, monkeypatch):
     monkeypatch.delenv("MRR_MAX_GRID")
     want = oracle.allreduce([bits(x) for x in ins], t, acc, tout)
     check_all(outs, want, tout, "walk n=%d %s/%s/%s grid %d" % (n, t, acc, tout, grid))
+
+
+@pytest.mark.parametrize("n,t,acc,tout", WALK_CASES, ids=["%d-%s-%s-%s" % c for c in WALK_CASES])
+def test_parity_persistent_grid(n, t, acc, tout, monkeypatch):
+    """MRR_LDS_CAP=0 (read per call): no LDS reservation, a persistent grid of
+    the table's workgroups per CU striding over the tiles."""
+    count = n * 64 * 2 * (3 * 512 // n + 1) * (16 // OUT_SIZE[tout]) + 13
+    announce("rsag persistent grid", n, t, acc, tout, count)
+    ins = inputs_for(t, n, count, seed0=90 * n + 1)
+    monkeypatch.setenv("MRR_LDS_CAP", "0")
+    outs = run(ins, t, acc, tout)
+    monkeypatch.delenv("MRR_LDS_CAP")
+    want = oracle.allreduce([bits(x) for x in ins], t, acc, tout)
+    check_all(outs, want, tout, "persistent n=%d %s/%s/%s" % (n, t, acc, tout))
