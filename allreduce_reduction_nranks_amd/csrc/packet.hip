@@ -109,23 +109,33 @@ struct ListedSources {  // one pointer per source
 };
 
 // Waits until every pending packet (bit s of pending[p]: source s of packet
-// kp[p]) carries `flag`, filling w[p][s] with the payloads.  Wavefront-uniform:
-// all lanes leave together.  Returns false after max_spins rounds (0 = none).
+// p) carries `flag`, filling w[p][s] with the payloads.  Each round loads
+// packet kq[p] of all N sources before any flag is looked at, then waits once:
+// a round costs one memory round trip, not one per source.  (Loading each
+// source under the lane's pending bit made the compiler wait after every
+// load: N round trips per round.)  kq[p] is the lane's packet index, or any
+// in-bounds index for a lane with nothing pending; the self slot of an inbox
+// exists and is loaded like the others.  Wavefront-uniform: all lanes leave
+// together.  Returns false after max_spins rounds (0 = none).
 template <int N, int P, typename Src>
-__device__ __forceinline__ bool poll_batch(const Src& src, const uint64_t* kp, uint32_t* pending,
+__device__ __forceinline__ bool poll_batch(const Src& src, const uint64_t* kq, uint32_t* pending,
                                            uint32_t (*w)[N], uint32_t flag, uint32_t max_spins) {
   uint32_t spins = 0;
   while (true) {
+    uint64_t pk[P][N];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+      for (int s = 0; s < N; ++s) pk[p][s] = ld_pkt(src(s) + kq[p]);
+    }
     uint32_t left = 0;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
 #pragma unroll
       for (int s = 0; s < N; ++s) {
-        if (pending[p] & (1u << s)) {
-          const uint64_t pk = ld_pkt(src(s) + kp[p]);
-          w[p][s] = (uint32_t)pk;
-          if ((uint32_t)(pk >> 32) == flag) pending[p] &= ~(1u << s);
-        }
+        const bool want = (pending[p] >> s) & 1u;
+        w[p][s] = want ? (uint32_t)pk[p][s] : w[p][s];
+        if (want && (uint32_t)(pk[p][s] >> 32) == flag) pending[p] &= ~(1u << s);
       }
       left |= pending[p];
     }
@@ -161,15 +171,16 @@ __global__ void __launch_bounds__(kPktMaxThreads) packet_allpair_k(const PacketA
   const StridedSources inbox{a.scratch + (uint64_t)d * N * a.npkt, a.npkt};
   const uint64_t step = (uint64_t)blockDim.x * P;
   for (uint64_t kb = k_lo; kb < k_hi; kb += step) {
-    uint64_t kp[P];
+    uint64_t kp[P], kq[P];
     uint32_t pending[P];
     uint32_t w[P][N];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       kp[p] = kb + (uint64_t)p * blockDim.x + threadIdx.x;
       pending[p] = kp[p] < k_hi ? peer_mask<N>(d) : 0u;
+      kq[p] = kp[p] < k_hi ? kp[p] : k_hi - 1;
     }
-    if (!poll_batch<N, P>(inbox, kp, pending, w, F, a.max_spins)) {
+    if (!poll_batch<N, P>(inbox, kq, pending, w, F, a.max_spins)) {
       report_timeout(a.dev_err);
       break;
     }
@@ -234,10 +245,11 @@ __global__ void __launch_bounds__(kPktMaxThreads) packet_rsag_k(const PacketRsag
   bool ok = true;
   for (uint64_t kb = k_lo; kb < k_hi && ok; kb += blockDim.x) {
     uint64_t kp[1] = {kb + threadIdx.x};
+    const uint64_t kq[1] = {kp[0] < k_hi ? kp[0] : k_hi - 1};
     const bool active = kp[0] < k_hi && wd0 + kp[0] < a.nwords;
     uint32_t pending[1] = {active ? peer_mask<N>(d) : 0u};
     uint32_t w[1][N];
-    ok = poll_batch<N, 1>(StridedSources{rs + (uint64_t)d * N * cw, cw}, kp, pending, w, F,
+    ok = poll_batch<N, 1>(StridedSources{rs + (uint64_t)d * N * cw, cw}, kq, pending, w, F,
                           a.max_spins);
     if (!ok) {
       report_timeout(a.dev_err);
@@ -257,6 +269,7 @@ __global__ void __launch_bounds__(kPktMaxThreads) packet_rsag_k(const PacketRsag
   // 3. all-gather receive
   for (uint64_t kb = k_lo; kb < k_hi && ok; kb += blockDim.x) {
     uint64_t kp[1] = {kb + threadIdx.x};
+    const uint64_t kq[1] = {kp[0] < k_hi ? kp[0] : k_hi - 1};
     uint32_t pending[1] = {0u};
     if (kp[0] < k_hi) {
 #pragma unroll
@@ -265,7 +278,7 @@ __global__ void __launch_bounds__(kPktMaxThreads) packet_rsag_k(const PacketRsag
     }
     const uint32_t want = pending[0];
     uint32_t w[1][N];
-    ok = poll_batch<N, 1>(StridedSources{ag + (uint64_t)d * N * cw, cw}, kp, pending, w, F,
+    ok = poll_batch<N, 1>(StridedSources{ag + (uint64_t)d * N * cw, cw}, kq, pending, w, F,
                           a.max_spins);
     if (!ok) {
       report_timeout(a.dev_err);
@@ -288,15 +301,16 @@ __global__ void __launch_bounds__(256) packet_reduce_k(const PacketReduceArgs a)
   constexpr int P = pkt_batch(N);
   const uint64_t step = (uint64_t)gridDim.x * blockDim.x * P;
   for (uint64_t kb = (uint64_t)blockIdx.x * blockDim.x * P; kb < a.npkts; kb += step) {
-    uint64_t kp[P];
+    uint64_t kp[P], kq[P];
     uint32_t pending[P];
     uint32_t w[P][N];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       kp[p] = kb + (uint64_t)p * blockDim.x + threadIdx.x;
       pending[p] = kp[p] < a.npkts ? peer_mask<N>((uint32_t)N) : 0u;
+      kq[p] = kp[p] < a.npkts ? kp[p] : a.npkts - 1;
     }
-    if (!poll_batch<N, P>(ListedSources{a.in}, kp, pending, w, a.flag_in, a.max_spins)) {
+    if (!poll_batch<N, P>(ListedSources{a.in}, kq, pending, w, a.flag_in, a.max_spins)) {
       report_timeout(a.dev_err);
       break;
     }
