@@ -25,7 +25,7 @@
 //     rank group together (non-temporal: the data is touched once),
 //     accumulates in rank order 0..N-1, narrows once and stores the result
 //     to all N outputs (the all-gather) with non-temporal 16-byte stores;
-//   - few waves per CU stream best (four to twelve single-wave workgroups
+//   - few waves per CU stream best (two to twelve single-wave workgroups
 //     per CU, see the launch-shape table below): more loads in flight thrash
 //     DRAM rows across the 2N same-offset buffers, fewer leave HBM latency
 //     exposed.  The cap is enforced by giving each workgroup an LDS
@@ -57,8 +57,7 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup
 //                             N=4 0.82 / 0.80, N=8 0.81 (f16) / 0.77,
 //                             N=16 0.78 / 0.76, N=32 - / 0.71)
 //   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: FP8 out U=1 x8 (E4M3FN out x6),
-//                             f16 out U=1 x6, f32 out U=2 x6 (E4M3FN x4: its
-//                             cheaper decode wants fewer waves);
+//                             f16 out U=1 x6, f32 out U=2 x6 (E4M3FN x4);
 //                             N=2: U=4 times 2 for f16 and 4 for f32 outputs
 //                             (a lane loads 16 bytes per rank); workgroups per
 //                             CU (2-8 swept at 32 MiB per rank) E4M3B15: 8 for
