@@ -73,6 +73,7 @@ def load_library() -> ctypes.CDLL:
             "mrr_fp8b15_to_f32": ([vp, vp, sz, vp], i),
             "mrr_f16_to_fp8b15": ([vp, vp, sz, vp], i),
             "mrr_f32_to_fp8b15": ([vp, vp, sz, vp], i),
+            "mrr_stream_copy": ([vp, vp, sz, vp], i),
             "mrr_rank_buffer_pitch": ([sz, i], sz),
             "mrr_status_string": ([i], ctypes.c_char_p),
             "mrr_version": ([], i),
@@ -244,3 +245,7 @@ def mrr_f16_to_fp8b15(src, dst, n, stream=None) -> int:
 
 def mrr_f32_to_fp8b15(src, dst, n, stream=None) -> int:
     return load_library().mrr_f32_to_fp8b15(_ptr(src), _ptr(dst), n, _stream(stream))
+
+
+def mrr_stream_copy(src, dst, nbytes, stream=None) -> int:
+    return load_library().mrr_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream))

@@ -155,6 +155,12 @@ static int max_resident_blocks(const void* kernel, int threads) {
 
 }  // namespace mrr
 
+namespace mrr {
+// calib.hip: plain copy on the RS/AG launch scheme; src/dst 16-byte aligned
+// and disjoint (checked by mrr_stream_copy).
+hipError_t launch_stream_copy(const void* src, void* dst, size_t nbytes, hipStream_t stream);
+}  // namespace mrr
+
 using namespace mrr;
 
 extern "C" {
@@ -519,6 +525,18 @@ mrr_status mrr_f16_to_fp8b15(const uint16_t* in, uint8_t* out, size_t n, void* s
 }
 mrr_status mrr_f32_to_fp8b15(const float* in, uint8_t* out, size_t n, void* stream) {
   return codec(3, in, 4, out, 1, n, stream, "mrr_f32_to_fp8b15");
+}
+
+mrr_status mrr_stream_copy(const void* src, void* dst, size_t nbytes, void* stream) {
+  const char* fn = "mrr_stream_copy";
+  if (nbytes == 0) return MRR_OK;
+  if (!src || !dst) return refuse(MRR_EINVAL, fn, "null pointer");
+  if (nbytes > ((size_t)1 << 40)) return refuse(MRR_EINVAL, fn, "nbytes over 1 TiB");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return refuse(MRR_EALIGN, fn, "16-byte alignment");
+  const Range i{(uintptr_t)src, (uintptr_t)src + nbytes};
+  const Range o{(uintptr_t)dst, (uintptr_t)dst + nbytes};
+  if (overlaps(i, o)) return refuse(MRR_EOVERLAP, fn, "src overlaps dst");
+  return hip_status(launch_stream_copy(src, dst, nbytes, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

@@ -142,14 +142,36 @@ def use_graph(args, alg_bytes):
     return args.graph == "on" or (args.graph == "auto" and alg_bytes < 64 * MiB)
 
 
-def copy_ceiling(torch, nbytes, steps=10):
-    """A plain device copy of nbytes (read nbytes + write nbytes) for context."""
+def copy_ceiling(torch, mrr, nbytes, steps=10):
+    """Two plain device copies of nbytes (read nbytes + write nbytes), in GB/s:
+    torch's copy_, and mrr_stream_copy, the library's copy on the launch
+    scheme of its reduction kernels (the same 1:1 read/write mix without the
+    arithmetic, so the practical ceiling a reduction is read against)."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
-    wall, kern = Timer(torch).run(lambda: b.copy_(a), steps, 3)
+    _, kern = Timer(torch).run(lambda: b.copy_(a), steps, 3)
+    torch_gbps = 2 * nbytes / (kern * 1e-3) / 1e9
+
+    def stream_copy():
+        st = mrr.mrr_stream_copy(a, b, nbytes)
+        if st != mrr.MRR_OK:
+            raise mrr.MrrError(st, "mrr_stream_copy")
+
+    _, kern = Timer(torch).run(stream_copy, max(steps, 20), 3)
+    stream_gbps = 2 * nbytes / (kern * 1e-3) / 1e9
     del a, b
-    return 2 * nbytes / (kern * 1e-3) / 1e9
+    return torch_gbps, stream_gbps
+
+
+def add_ceilings(result, ceilings, achieved):
+    """Copy-ceiling figures into the JSON config (see copy_ceiling)."""
+    if ceilings is None:
+        return
+    torch_gbps, stream_gbps = ceilings
+    result["config"]["copy_ceiling_gbps"] = round(torch_gbps, 2)
+    result["config"]["stream_copy_gbps"] = round(stream_gbps, 2)
+    result["config"]["frac_of_stream_copy"] = round(achieved / stream_gbps, 4)
 
 
 def cpu_baseline_rsag(ins_dev, t, acc, tout, sample_elems):
@@ -255,7 +277,7 @@ def bench_rsag(args, torch, mrr, synth):
            "c4": "rsag_8x32MiB_%s_to_%s" % (t, tout), "c5": "rsag_%dx256MiB_bf16" % n,
            "custom": "rsag_%dx%dKiB_%s" % (n, args.size, t)}[args.config]
     traffic = measured_traffic(key)
-    ceiling = copy_ceiling(torch, n * count * ESIZE[t]) if args.copy_ceiling else None
+    ceiling = copy_ceiling(torch, mrr, n * count * ESIZE[t]) if args.copy_ceiling else None
     workload = {"c1": "RS/AG allreduce, 2 ranks x 1 MiB bf16 ~N(0,1), fp32 accumulation",
                 "c2": "RS/AG zero-copy allreduce, 8 ranks x 64 MiB f16 ~N(0,1), fp32 accumulation, "
                       "reduced chunks written to all 8 outputs",
@@ -279,8 +301,7 @@ def bench_rsag(args, torch, mrr, synth):
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": traffic},
     }
-    if ceiling is not None:
-        result["config"]["copy_ceiling_gbps"] = round(ceiling, 2)
+    add_ceilings(result, ceiling, achieved)
     if sep_us is not None:
         result["config"]["kernel_us_one_allocation_per_rank"] = round(sep_us, 2)
     result["config"]["timing"] = TIMING_GRAPH if graph else TIMING_EAGER
@@ -394,7 +415,7 @@ def bench_dual(args, torch, mrr, synth):
                      "traffic": measured_traffic(key)},
     }
     if args.copy_ceiling:
-        result["config"]["copy_ceiling_gbps"] = round(copy_ceiling(torch, n * count), 2)
+        add_ceilings(result, copy_ceiling(torch, mrr, n * count), achieved)
     if args.cpu_baseline:
         import oracle
         sample = min(count, args.cpu_sample)
@@ -442,7 +463,7 @@ def bench_codec(args, torch, mrr, synth):
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     key = "codec_%s_256Mi" % args.dir
-    ceiling = copy_ceiling(torch, n * ESIZE[tin]) if args.copy_ceiling else None
+    ceiling = copy_ceiling(torch, mrr, n * ESIZE[tin]) if args.copy_ceiling else None
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
@@ -458,8 +479,7 @@ def bench_codec(args, torch, mrr, synth):
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": measured_traffic(key, CODEC_SOURCES)},
     }
-    if ceiling is not None:
-        result["config"]["copy_ceiling_gbps"] = round(ceiling, 2)
+    add_ceilings(result, ceiling, achieved)
     if args.cpu_baseline:
         import oracle
         sample = min(n, args.cpu_sample)

@@ -309,6 +309,19 @@ mrr_status mrr_f16_to_fp8b15(const uint16_t* in, uint8_t* out, size_t n, void* s
 mrr_status mrr_f32_to_fp8b15(const float* in, uint8_t* out, size_t n, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Copy-kernel calibration (measurement aid, not part of the reduction).
+ * Copies nbytes from src to dst with the launch scheme of the RS/AG kernels
+ * (one single-wave workgroup per tile, residency capped through an unused
+ * LDS reservation, non-temporal 16-byte loads and stores): the same 1:1 mix
+ * of streaming reads and writes as a reduction, without its arithmetic, so
+ * its bandwidth is the practical ceiling a reduction is read against.
+ * src and dst: device pointers, 16-byte aligned (MRR_EALIGN), ranges
+ * disjoint (MRR_EOVERLAP); nbytes == 0 launches nothing; nbytes over 1 TiB
+ * -> MRR_EINVAL.  Stream-ordered and asynchronous; allocates nothing.
+ * ------------------------------------------------------------------------ */
+mrr_status mrr_stream_copy(const void* src, void* dst, size_t nbytes, void* stream);
+
+/* --------------------------------------------------------------------------
  * HBM placement of the simulated rank buffers (one GPU holds all N).
  *
  * When the N same-size rank buffers of one side (inputs, or outputs) are

@@ -177,6 +177,16 @@ def test_codec_checks(lib):
     assert mrr.mrr_f16_to_fp8b15(fake(0), fake(1), 0, 0) == mrr.MRR_OK
 
 
+def test_stream_copy_checks(lib):
+    assert mrr.mrr_stream_copy(fake(0), fake(1), 0, 0) == mrr.MRR_OK  # nothing to do
+    assert mrr.mrr_stream_copy(0, fake(1), 64, 0) == mrr.MRR_EINVAL
+    assert mrr.mrr_stream_copy(fake(0, off=8), fake(1), 64, 0) == mrr.MRR_EALIGN
+    assert mrr.mrr_stream_copy(fake(0), fake(1, off=4), 64, 0) == mrr.MRR_EALIGN
+    assert mrr.mrr_stream_copy(fake(0), fake(0, off=32), 64, 0) == mrr.MRR_EOVERLAP
+    assert mrr.mrr_stream_copy(fake(0), fake(0), 64, 0) == mrr.MRR_EOVERLAP
+    assert mrr.mrr_stream_copy(fake(0), fake(1), (1 << 40) + 16, 0) == mrr.MRR_EINVAL
+
+
 def test_binding_names_match_header():
     names = declared_functions()
     for n in names:
