@@ -207,6 +207,12 @@ mrr_status mrr_allreduce_rsag_dual(const void* const* inputs, void* const* outpu
  *           (every workgroup waits for its peers), else MRR_EINVAL.
  * Calls that overlap in time on the same scratch or flags race; calls on one
  * stream never overlap.
+ * Co-residency is checked against an idle GPU.  Work running at the same time
+ * on other streams (an RS/AG call, whose workgroups also hold LDS, or any
+ * other kernel) only delays the packet workgroups that do not fit until it
+ * drains.  But two packet calls running at the same time on different
+ * streams can each hold workgroups that wait for peers the other keeps off
+ * the GPU: order such calls on one stream, or give them a max_spins bound.
  * ------------------------------------------------------------------------ */
 /* Scratch and flag sizes for the calls above; 0 for an unknown type, nranks
  * outside [1, 32], or a count the entry points refuse as too large. */
