@@ -43,7 +43,7 @@
 
 namespace mrr {
 
-constexpr int kRsagThreads = 64;  // one wave per workgroup
+constexpr int kRsagThreads = 64;  // one wave per workgroup (all kernels but one shape below)
 
 // Launch shape, from sweeps of (units per lane U) x (workgroups per CU) of
 // this kernel on MI355X at 64 MiB and 256 MiB per rank (16- and 32-bit
@@ -57,7 +57,8 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup
 //                             N=4 0.82 / 0.80, N=8 0.81 (f16) / 0.77,
 //                             N=16 0.78 / 0.76, N=32 - / 0.71)
 //   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: FP8 out U=1 x8 (E4M3FN out x6),
-//                             f16 out U=1 x6, f32 out U=2 x6 (E4M3FN x4);
+//                             f16 out U=1 x6, f32 out U=2 (128-lane tiles,
+//                             below) x4 (E4M3FN x2);
 //                             N=2: U=4 times 2 for f16 and 4 for f32 outputs
 //                             (a lane loads 16 bytes per rank); workgroups per
 //                             CU (2-8 swept at 32 MiB per rank) E4M3B15: 8 for
@@ -65,6 +66,14 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup
 //                             out, 4 for f16, 2 for f32.
 //   One-pass FP8 -> f16 + FP8 (rsag_dual_kernel): U=2 x4 (U=8 x4 at N=2; 2-8
 //                             swept at 8 x 32 MiB and 2 x 32 MiB).
+//   Workgroup width: 64 lanes, except FP8 inputs with f32 outputs above two
+//   ranks, which run two-wave (128-lane) tiles at 4 (E4M3B15) or 2 (E4M3FN)
+//   workgroups per CU: 8 x 32 MiB E4M3B15 0.69 -> 0.72 of the HBM peak,
+//   E4M3FN 0.68 -> 0.75.  Wider tiles lost elsewhere (FP8 and one-pass
+//   outputs, 16-bit data at 2, 8 and 32 ranks).
+constexpr int rsag_threads(int n, int tin, int tout) {
+  return is_fp8(tin) && tout == kF32 && n > 2 ? 128 : kRsagThreads;
+}
 constexpr int rsag_unroll(int n, int tin, int tout) {
   if (is_fp8(tin)) {
     if (n == 2) return 4 * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
@@ -78,7 +87,7 @@ constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
       if (tin == kFP8FN) return tout == kF32 ? 2 : tout == kF16 ? 4 : 8;
       return tout == kF16 ? 6 : 8;
     }
-    if (tout == kF32) return tin == kFP8FN ? 4 : 6;
+    if (tout == kF32) return tin == kFP8FN ? 2 : 4;  // 128-lane workgroups
     return tout == kFP8 ? 8 : 6;
   }
   return n == 2 ? 12 : n == 4 ? 8 : n == 8 ? 8 : n == 16 ? 4 : 8;
@@ -114,7 +123,7 @@ template <int In, int Out> struct Unit {
   static constexpr int EPW = 4 / Ty<In>::size;  // elements per input word
 };
 
-// Reduces UU units v0 + u * kRsagThreads (u < UU) over the N ranks and stores
+// Reduces UU units v0 + u * T (u < UU; T lanes per workgroup) over the N ranks and stores
 // each result to all N outputs.  The first partial sum is x_0 rounded to the
 // accumulator type (the identity except for an FP8 accumulator, which
 // saturates an infinite x_0 like any later sum).  Ranks are taken in groups
@@ -128,7 +137,7 @@ template <int In, int Out> struct Unit {
 //
 // Out2 != 0 (FP8 types only, with Out = f16): each unit's 8 sums are also
 // encoded to Out2 and stored, 8 bytes per lane, to out2[0..N-1].
-template <int N, int In, int Acc, int Out, int UU, int G, int Out2 = 0>
+template <int N, int In, int Acc, int Out, int UU, int G, int Out2 = 0, int T = kRsagThreads>
 __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
                                              void* const* out2 = nullptr) {
   constexpr int UE = Unit<In, Out>::UE;
@@ -146,7 +155,7 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
 #pragma unroll
-      for (int r = 0; r < G; ++r) ld_words<D>(a.in[g + r], v0 + (uint64_t)u * kRsagThreads, raw[u][r]);
+      for (int r = 0; r < G; ++r) ld_words<D>(a.in[g + r], v0 + (uint64_t)u * T, raw[u][r]);
     }
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
@@ -176,7 +185,7 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
   }
 #pragma unroll
   for (int u = 0; u < UU; ++u) {
-    const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
+    const uint64_t v = v0 + (uint64_t)u * T;
     u32x4 o;
     if constexpr (Out == kFP8) o = special[u] ? encode16<kFP8>(acc[u]) : encode16_fp8_hw(acc[u]);
     else o = encode16<Out>(acc[u]);
@@ -193,7 +202,7 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
 }
 
 // The persistent tile loop shared by the single- and dual-output kernels.
-template <int N, int In, int Acc, int Out, int U, int Out2>
+template <int N, int In, int Acc, int Out, int U, int Out2, int T = kRsagThreads>
 __device__ __forceinline__ void rsag_vec_body(const RsagArgs& a, void* const* out2) {
   constexpr int G = rsag_group(N, In, Acc);
   for (uint32_t i = blockIdx.x; i < a.launch_tiles; i += gridDim.x) {
@@ -201,14 +210,14 @@ __device__ __forceinline__ void rsag_vec_body(const RsagArgs& a, void* const* ou
     const uint32_t tile = i - chunk_rel * a.tiles_per_chunk;
     const uint64_t v_lo = (uint64_t)(a.first_chunk + chunk_rel) * a.chunk_vecs;
     const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
-    const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
-    if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
-      reduce_store<N, In, Acc, Out, U, G, Out2>(a, v0, out2);
+    const uint64_t v0 = v_lo + (uint64_t)tile * (T * U) + threadIdx.x;
+    if (v0 + (uint64_t)(U - 1) * T < v_hi) {
+      reduce_store<N, In, Acc, Out, U, G, Out2, T>(a, v0, out2);
     } else {  // the last, partial tile of a chunk: unit by unit
 #pragma nounroll
       for (int u = 0; u < U; ++u) {
-        const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
-        if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G, Out2>(a, v, out2);
+        const uint64_t v = v0 + (uint64_t)u * T;
+        if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G, Out2, T>(a, v, out2);
       }
     }
   }
@@ -218,9 +227,9 @@ __device__ __forceinline__ void rsag_vec_body(const RsagArgs& a, void* const* ou
     reduce_elem<In, Acc, Out, Out2>(a.in, a.out, N, a.tail_begin + threadIdx.x, out2);
 }
 
-template <int N, int In, int Acc, int Out, int U>
-__global__ void __launch_bounds__(kRsagThreads) rsag_vec_kernel(const RsagArgs a) {
-  rsag_vec_body<N, In, Acc, Out, U, 0>(a, nullptr);
+template <int N, int In, int Acc, int Out, int U, int T>
+__global__ void __launch_bounds__(T) rsag_vec_kernel(const RsagArgs a) {
+  rsag_vec_body<N, In, Acc, Out, U, 0, T>(a, nullptr);
 }
 
 // FP8 inputs, f16 outputs plus the FP8 re-encode of the same sums.
@@ -402,12 +411,12 @@ static RsagShape rsag_shape(int wpc, uint32_t launch_tiles) {
 
 template <int In, int Acc, int Out>
 static void launch_vec_typed(int nranks, const RsagShape& sh, const RsagArgs& a, hipStream_t s) {
-  const dim3 block(kRsagThreads);
   switch (nranks) {
-#define MRR_CASE(N)                                                                        \
-  case N:                                                                                  \
-    hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In, Out)>), sh.grid, block, \
-                       sh.lds, s, a);                                                      \
+#define MRR_CASE(N)                                                                          \
+  case N:                                                                                    \
+    hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In, Out),            \
+                                        rsag_threads(N, In, Out)>),                          \
+                       sh.grid, dim3(rsag_threads(N, In, Out)), sh.lds, s, a);               \
     break;
     MRR_CASE(2) MRR_CASE(4) MRR_CASE(8) MRR_CASE(16) MRR_CASE(32)
 #undef MRR_CASE
@@ -515,7 +524,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
       a.in[r] = inputs[r];
       a.out[r] = outputs[r];
     }
-    rsag_geometry(p, vw, ue, (uint64_t)kRsagThreads * rsag_unroll(n, In, Out), a);
+    rsag_geometry(p, vw, ue, (uint64_t)rsag_threads(n, In, Out) * rsag_unroll(n, In, Out), a);
     // Small calls: when the table's U would leave fewer than 2 tiles per CU,
     // CUs sit idle; the runtime-N kernel at one unit group per lane spreads
     // the same work over U times more workgroups (measured under HIP-graph
