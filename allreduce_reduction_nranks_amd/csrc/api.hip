@@ -315,16 +315,17 @@ static mrr_status packet_checks(const char* fn, const void* const* inputs, void*
   return MRR_OK;
 }
 
-// Blocks per rank: the caller's, or one poll round per lane over `units`
-// words, capped by the workgroups the GPU holds at once and by the flag slots.
+// Blocks per rank: the caller's, or one poll round per lane (of `batch`
+// packets) over `units` words, capped by the workgroups the GPU holds at once
+// and by the flag slots.
 static mrr_status packet_geometry(const char* fn, const void* kernel, int nranks, uint64_t units,
-                                  int threads, int blocks_per_rank, int* B) {
+                                  int threads, int batch, int blocks_per_rank, int* B) {
   const int resident = max_resident_blocks(kernel, threads);
   if (resident <= 0) return hip_status(hipErrorInvalidDevice, fn);
   const int max_b = resident / nranks;
   int b = blocks_per_rank;
   if (b == 0) {
-    const uint64_t per_block = (uint64_t)threads * packet_batch(nranks);
+    const uint64_t per_block = (uint64_t)threads * (uint64_t)batch;
     const uint64_t want = (units + per_block - 1) / per_block;
     b = (int)(want < 1 ? 1 : (want > (uint64_t)MRR_PKT_FLAG_SLOTS ? MRR_PKT_FLAG_SLOTS : want));
     if (b > max_b) b = max_b;
@@ -351,7 +352,8 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   const uint64_t npkt = (nbytes + 3) / 4;
   const int T = threads ? threads : 64;
   int B = 0;
-  st = packet_geometry(fn, packet_allpair_kernel(nranks, t, tacc), nranks, npkt, T,
+  const int batch = packet_allpair_batch(nranks, npkt);
+  st = packet_geometry(fn, packet_allpair_kernel(nranks, t, tacc, batch), nranks, npkt, T, batch,
                        blocks_per_rank, &B);
   if (st != MRR_OK) return st;
   PacketArgs a = {};
@@ -367,7 +369,7 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   a.pkts_per_block = (npkt + (uint64_t)B - 1) / (uint64_t)B;
   a.nblocks = (uint32_t)B;
   a.max_spins = max_spins;
-  return hip_status(launch_packet_allpair(a, nranks, t, tacc, T, (hipStream_t)stream), fn);
+  return hip_status(launch_packet_allpair(a, nranks, t, tacc, T, batch, (hipStream_t)stream), fn);
 }
 
 // Payload words per full chunk of the two-phase packet allreduce: the RS/AG
@@ -400,7 +402,8 @@ mrr_status mrr_allreduce_packet_rsag(const void* const* inputs, void* const* out
   const uint64_t cw = rsag_chunk_words(count, e, nranks);
   const int T = threads ? threads : 64;
   int B = 0;
-  st = packet_geometry(fn, packet_rsag_kernel(nranks, t, tacc), nranks, cw, T, blocks_per_rank, &B);
+  st = packet_geometry(fn, packet_rsag_kernel(nranks, t, tacc), nranks, cw, T, 1, blocks_per_rank,
+                       &B);
   if (st != MRR_OK) return st;
   PacketRsagArgs a = {};
   for (int r = 0; r < nranks; ++r) {

@@ -107,14 +107,14 @@ struct PacketReduceArgs {
 };
 
 bool packet_supported(int nranks, int t, int tacc);
-// Packets per lane that one poll round of the allpair / reduce kernels covers.
-int packet_batch(int nranks);
+// Packets per lane that one poll round of the allpair kernel covers (1 or 2).
+int packet_allpair_batch(int nranks, uint64_t npkt);
 // Largest workgroup size the allpair kernel is built for.
 int packet_max_threads();
-// Pointer to the allpair kernel for (nranks, t, tacc), used for occupancy.
-const void* packet_allpair_kernel(int nranks, int t, int tacc);
+// Pointer to the allpair kernel for (nranks, t, tacc, batch), used for occupancy.
+const void* packet_allpair_kernel(int nranks, int t, int tacc, int batch);
 hipError_t launch_packet_allpair(const PacketArgs& a, int nranks, int t, int tacc, int threads,
-                                 hipStream_t stream);
+                                 int batch, hipStream_t stream);
 hipError_t launch_packet_reduce(const PacketReduceArgs& a, int nranks, int t, int tacc,
                                 hipStream_t stream);
 const void* packet_rsag_kernel(int nranks, int t, int tacc);

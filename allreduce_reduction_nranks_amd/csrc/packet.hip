@@ -82,11 +82,19 @@ __device__ __forceinline__ void report_timeout(uint32_t* dev_err) {
   if (dev_err) atomicCAS(dev_err, 0u, (uint32_t)MRR_ETIMEDOUT);
 }
 
-// Packets per lane handled in one poll round (all P x (N - 1) loads in flight
-// together).  Measured on MI355X: one packet per lane and more workgroups
-// beats batching, which costs registers and therefore co-resident
-// workgroups; the latency of a call is set by how many CUs take part.
+// Packets per lane handled in one poll round (all P x N loads in flight
+// together).  The receive-only and two-phase kernels take one.  The allpair
+// kernel takes one, or two for calls of at least kPktBatch2Min packets per
+// rank at N <= 8: measured on MI355X, 8 ranks of f16, per call under graph
+// replay, two per lane cost 16 KiB 5.7 -> 9.0 us and 64 KiB 8.7 -> 10.7 us
+// (half as many workgroups share the polling), gained 256 KiB 27.2 ->
+// 20.9 us (one per lane needs more workgroups than fit, so lanes poll twice
+// in sequence) and tied at 1 MiB; four per lane lost at every size.
 constexpr int pkt_batch(int) { return 1; }
+constexpr uint64_t kPktBatch2Min = 32768;
+int packet_allpair_batch(int nranks, uint64_t npkt) {
+  return nranks <= 8 && npkt >= kPktBatch2Min ? 2 : 1;
+}
 // Largest workgroup of the allpair kernel (bounds its registers at 256).
 constexpr int kPktMaxThreads = 512;
 int packet_max_threads() { return kPktMaxThreads; }
@@ -145,9 +153,8 @@ __device__ __forceinline__ bool poll_batch(const Src& src, const uint64_t* kq, u
   }
 }
 
-template <int N, int T, int Acc>
+template <int N, int T, int Acc, int P>
 __global__ void __launch_bounds__(kPktMaxThreads) packet_allpair_k(const PacketArgs a) {
-  constexpr int P = pkt_batch(N);
   const uint32_t d = blockIdx.x % N;
   const uint32_t b = blockIdx.x / N;
   uint32_t* const my_flags = a.flags + (uint64_t)d * kFlagSlots;
@@ -354,32 +361,55 @@ bool packet_supported(int nranks, int t, int tacc) {
   return false;
 }
 
-const void* packet_allpair_kernel(int nranks, int t, int tacc) {
+// Rank counts with a two-packets-per-lane allpair kernel (packet_allpair_batch).
+#define MRR_PKT_RANKS_P2(X, T, A) X(2, T, A) X(4, T, A) X(8, T, A)
+
+const void* packet_allpair_kernel(int nranks, int t, int tacc, int batch) {
 #define MRR_K(N, T, A) \
-  if (nranks == N && t == T && tacc == A) return (const void*)&packet_allpair_k<N, T, A>;
+  if (nranks == N && t == T && tacc == A) return (const void*)&packet_allpair_k<N, T, A, 1>;
+#define MRR_K2(N, T, A) \
+  if (nranks == N && t == T && tacc == A) return (const void*)&packet_allpair_k<N, T, A, 2>;
 #define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
+#define MRR_ALLN2(T, A) MRR_PKT_RANKS_P2(MRR_K2, T, A)
+  if (batch == 2) {
+    MRR_PKT_PAIRS(MRR_ALLN2)
+    return nullptr;
+  }
   MRR_PKT_PAIRS(MRR_ALLN)
+#undef MRR_ALLN2
 #undef MRR_ALLN
+#undef MRR_K2
 #undef MRR_K
   return nullptr;
 }
 
 hipError_t launch_packet_allpair(const PacketArgs& a, int nranks, int t, int tacc, int threads,
-                                 hipStream_t stream) {
+                                 int batch, hipStream_t stream) {
   const dim3 grid((uint32_t)nranks * a.nblocks), block((uint32_t)threads);
 #define MRR_K(N, T, A)                                                               \
   if (nranks == N && t == T && tacc == A) {                                          \
-    hipLaunchKernelGGL((packet_allpair_k<N, T, A>), grid, block, 0, stream, a);      \
+    hipLaunchKernelGGL((packet_allpair_k<N, T, A, 1>), grid, block, 0, stream, a);   \
+    return hipGetLastError();                                                        \
+  }
+#define MRR_K2(N, T, A)                                                              \
+  if (nranks == N && t == T && tacc == A) {                                          \
+    hipLaunchKernelGGL((packet_allpair_k<N, T, A, 2>), grid, block, 0, stream, a);   \
     return hipGetLastError();                                                        \
   }
 #define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
+#define MRR_ALLN2(T, A) MRR_PKT_RANKS_P2(MRR_K2, T, A)
+  if (batch == 2) {
+    MRR_PKT_PAIRS(MRR_ALLN2)
+    return hipErrorInvalidValue;
+  }
   MRR_PKT_PAIRS(MRR_ALLN)
+#undef MRR_ALLN2
 #undef MRR_ALLN
+#undef MRR_K2
 #undef MRR_K
   return hipErrorInvalidValue;
 }
 
-int packet_batch(int nranks) { return pkt_batch(nranks); }
 
 hipError_t launch_packet_reduce(const PacketReduceArgs& a, int nranks, int t, int tacc,
                                 hipStream_t stream) {

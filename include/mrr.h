@@ -83,8 +83,8 @@ typedef enum mrr_dtype {
 
 /* Packet / RS-AG crossover for mrr_allreduce, measured on one MI355X: 0.
  * There RS/AG is faster at every size (8 ranks of f16, per call under HIP
- * graph replay: 1.9 us against 5.7-8.7 us for allpair packets at 16-64 KiB
- * per rank, 3.6 us against 47.9 us at 1 MiB), because within one GPU it
+ * graph replay: 1.9 us against 5.7-8.8 us for allpair packets at 16-64 KiB
+ * per rank, 3.6 us against 47.3 us at 1 MiB), because within one GPU it
  * needs no cross-rank synchronisation while packets double the bytes moved.
  * The pages' selectors, spanning GPUs, switch to RS/AG above 512 KiB
  * (Python default) or 2 MiB (NCCL shim). */

@@ -93,6 +93,24 @@ def test_allpair_types_ragged(n, t, acc):
         check_call(ins, outs, st, t, acc, it, copies, "n=%d %s/%s it %d" % (n, t, acc, it))
 
 
+# The allpair kernel polls two packets per lane from 32768 packets per rank up
+# (at most 8 ranks), one below: sizes on both sides of that switch, ragged
+# past it, and 16 ranks at the same size (one per lane).
+@pytest.mark.parametrize("n,npkt", [(2, 32767), (2, 32768), (4, 32768 + 129), (8, 32767),
+                                    (8, 32768), (8, 65536 + 3), (16, 32768 + 1)])
+@pytest.mark.parametrize("t,acc", [("f16", "f32"), ("fp8", "f16")])
+def test_allpair_packets_per_lane_switch(n, npkt, t, acc):
+    count = npkt * 4 // {"f16": 2, "fp8": 1}[t] - 1  # last word half (f16) or 3/4 (fp8) full
+    announce("packet allpair batch switch", n, npkt, t, acc, count)
+    st = PacketState(n, count, t)
+    outs = [empty(t, count, 0xEE) for _ in range(n)]
+    for it in (1, 2):
+        ins = inputs_for(t, n, count, seed0=11 * it + n, kind="fp8codes" if t == "fp8" else "uniform")
+        copies = [x.clone() for x in ins]
+        assert allpair(ins, outs, st, t, acc) == mrr.MRR_OK
+        check_call(ins, outs, st, t, acc, it, copies, "n=%d npkt=%d %s it %d" % (n, npkt, t, it))
+
+
 def test_geometry_changes_between_calls():
     """Blocks per rank and threads change every call; the shared flag slots
     keep every call consistent (no hang, flags advance by one per call)."""
