@@ -52,10 +52,12 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup (all kernels but one
 // channel and bank mapping -- so each entry is the setting that stayed near
 // the best across buffer sizes rather than a formula.
 //   16-bit and 32-bit inputs: N=2 U=2 x12, N=4 U=1 x8, N=8 U=1 x8,
-//                             N=16 U=1 x4, N=32 U=1 x8 (fractions of the HBM
-//                             peak at 64 / 256 MiB per rank: N=2 0.81 / 0.82,
-//                             N=4 0.82 / 0.80, N=8 0.81 (f16) / 0.77,
-//                             N=16 0.78 / 0.76, N=32 - / 0.71)
+//                             N=16 U=1 x4, N=32 U=1 x4 with loads in groups of
+//                             8 ranks (fractions of the HBM peak at 64 / 256 MiB
+//                             per rank: N=2 0.81 / 0.82, N=4 0.82 / 0.80,
+//                             N=8 0.81 (f16) / 0.77, N=16 0.78 / 0.76,
+//                             N=32 0.75 / 0.77; with groups of 16 ranks at 8
+//                             per CU, N=32 ran 0.70 / 0.70)
 //   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: FP8 out U=1 x8 (E4M3FN out x6),
 //                             f16 out U=1 x6, f32 out U=2 (128-lane tiles,
 //                             below) x4 (E4M3FN x2);
@@ -90,16 +92,18 @@ constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
     if (tout == kF32) return tin == kFP8FN ? 2 : 4;  // 128-lane workgroups
     return tout == kFP8 ? 8 : 6;
   }
-  return n == 2 ? 12 : n == 4 ? 8 : n == 8 ? 8 : n == 16 ? 4 : 8;
+  return n == 2 ? 12 : n == 4 ? 8 : n == 8 ? 8 : 4;
 }
 constexpr int rsag_dual_unroll(int n) { return n == 2 ? 8 : 2; }
 constexpr int rsag_dual_wg_per_cu(int) { return 4; }
 // Ranks whose vectors are loaded together before they are added: all of them
-// up to 16 ranks; groups of 16 above that, and groups of 8 for FP8 inputs or
-// an FP8 accumulator (16 values per vector and two decode paths make the
-// unrolled body large).
+// up to 16 ranks; groups of 8 above that (measured on MI355X at 32 ranks:
+// groups of 8 at 4 workgroups per CU 0.72-0.77 of the HBM peak at 32-256 MiB
+// per rank, against 0.66-0.70 for groups of 16 at 8 per CU and 0.54-0.57 at
+// 4 per CU), and groups of 8 for FP8 inputs or an FP8 accumulator (16 values
+// per vector and two decode paths make the unrolled body large).
 constexpr int rsag_group(int n, int tin, int tacc) {
-  return (is_fp8(tin) || is_fp8(tacc)) ? (n < 8 ? n : 8) : (n < 16 ? n : 16);
+  return (is_fp8(tin) || is_fp8(tacc)) ? (n < 8 ? n : 8) : (n <= 16 ? n : 8);
 }
 
 // Out2 != 0: the same sum is also written, as type Out2, to out2[0..n-1].
