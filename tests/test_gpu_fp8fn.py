@@ -82,21 +82,23 @@ def test_rsag_fn_unaligned_buffers():
         assert_bits_equal(bits(o), want, T, "out[%d]" % k)
 
 
-def test_rsag_fn_full_size_sampled():
-    """8 ranks x 64 MiB of E4M3FN, f32 accumulation, pooled layout, sampled."""
+@pytest.mark.parametrize("tout", [T, "f32"])
+def test_rsag_fn_full_size_sampled(tout):
+    """8 ranks x 64 MiB of E4M3FN, f32 accumulation, pooled layout, sampled;
+    E4M3FN outputs, and f32 outputs (the 128-lane-tile kernel)."""
     n, count = 8, 64 << 20
-    announce("fn rsag 8 x 64 MiB")
+    announce("fn rsag 8 x 64 MiB ->", tout)
     pool_in, ins = mrr.alloc_rank_buffers(n, count, T)
     for r, x in enumerate(inputs_for(T, n, count, seed0=7300, device="cuda")):
         ins[r].copy_(x)
-    pool_out, outs = mrr.alloc_rank_buffers(n, count, T)
-    assert mrr.mrr_allreduce_rsag_ex(ins, outs, count, T, "f32", T, n) == mrr.MRR_OK
+    pool_out, outs = mrr.alloc_rank_buffers(n, count, tout)
+    assert mrr.mrr_allreduce_rsag_ex(ins, outs, count, T, "f32", tout, n) == mrr.MRR_OK
     torch.cuda.synchronize()
     idx = torch.from_numpy(np.unique(np.concatenate([
         np.random.default_rng(8).integers(0, count, 1 << 17), [0, count - 1]]))).cuda()
-    want = oracle.allreduce([bits(x[idx]) for x in ins], T, "f32", T)
+    want = oracle.allreduce([bits(x[idx]) for x in ins], T, "f32", tout)
     for k in range(n):
-        assert_bits_equal(bits(outs[k][idx]), want, T, "out[%d]" % k)
+        assert_bits_equal(bits(outs[k][idx]), want, tout, "out[%d]" % k)
 
 
 @pytest.mark.parametrize("n", [3, 5, 12, 31])

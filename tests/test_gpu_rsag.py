@@ -257,7 +257,7 @@ def test_full_size_eight_ranks_64mib_f16():
         assert torch.equal(outs[k].view(torch.int16), outs[0].view(torch.int16))
 
 
-@pytest.mark.parametrize("tout", ["f16", "fp8"])
+@pytest.mark.parametrize("tout", ["f16", "fp8", "f32"])
 def test_full_size_fp8_eight_ranks_32mib(tout):
     n, count = 8, 32 * (1 << 20)
     announce("rsag 8x32MiB fp8 ->", tout)
