@@ -430,22 +430,22 @@ static void launch_vec_typed(int nranks, const RsagShape& sh, const RsagArgs& a,
 
 // The runtime-N kernel loads 16 bytes per lane per rank like the compiled
 // ones at N = 8, times a multiplier M of units per lane for 16- and 32-bit
-// inputs so that small rank counts still keep enough loads in flight.
-// Measured on MI355X (64-128 MiB per rank): M=4 for N <= 4, M=2 for N <= 8,
-// M=1 above; workgroups per CU (one per tile, capped as for the compiled
-// kernels, 4-16 swept at 64 MiB per rank): 12 for N <= 4, 4 above
-// (3 x f16 0.76 of the HBM peak, 6 x bf16 0.77, 12 x f16 0.78,
+// inputs (MRR_RSAG_ANY_M = 1, 2 or 4; the table uses 1).  Measured on MI355X
+// at 64 MiB per rank of bf16, M in {1,2,4} x 4-16 workgroups per CU (one per
+// tile, capped as for the compiled kernels): M=1 with 16 per CU for N <= 4
+// (3 ranks 0.81 of the HBM peak; the persistent-grid table, M=4 at 12 per
+// CU, gave 0.76), 8 per CU for N <= 8 (5, 6, 7 ranks 0.81, 0.80, 0.80,
+// against 0.74-0.77 at M=2 and 4 per CU), 4 per CU above (12 x f16 0.78,
 // 24 x bf16 0.73).  FP8 inputs keep M=1 and 6 per CU.
 // MRR_RSAG_ANY_M and MRR_RSAG_WPC override.
 constexpr int rsag_any_unroll(int tin, int tout) {
   return is_fp8(tin) ? (tout == kF32 ? 4 : tout == kF16 ? 2 : 1) : 1;
 }
-static int rsag_any_multiplier(int n) { return n <= 4 ? 4 : n <= 8 ? 2 : 1; }
+static int rsag_any_multiplier(int) { return 1; }
 static int rsag_any_wg_per_cu(int n, int tin) {
   if (is_fp8(tin)) return 6;
-  return n <= 4 ? 12 : 4;
+  return n <= 4 ? 16 : n <= 8 ? 8 : 4;
 }
-
 template <int In, int Acc, int Out>
 static void launch_any_typed(int n, int mult, const RsagShape& sh, const RsagArgs& a,
                              hipStream_t s) {
