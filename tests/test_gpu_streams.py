@@ -122,3 +122,14 @@ def test_graph_of_dispatcher_dual_and_codec():
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "replay %d buffer %d" % (rep, i)
     want = oracle.allreduce([bits(x) for x in ins5], "f16", "f32")
     assert_bits_equal(bits(eager[0][0]), want, "f16", "dispatcher vs oracle")
+
+
+def test_default_stream_is_torch_current_stream():
+    """stream=None resolves to torch's current stream on the current device,
+    inside and outside a torch.cuda.stream context."""
+    import allreduce_reduction_nranks_amd as mrr_mod
+    assert mrr_mod._stream(None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert mrr_mod._stream(None) == s.cuda_stream
+    assert mrr_mod._stream(None) == torch.cuda.current_stream().cuda_stream
