@@ -436,14 +436,17 @@ static void launch_vec_typed(int nranks, const RsagShape& sh, const RsagArgs& a,
 // (3 ranks 0.81 of the HBM peak; the persistent-grid table, M=4 at 12 per
 // CU, gave 0.76), 8 per CU for N <= 8 (5, 6, 7 ranks 0.81, 0.80, 0.80,
 // against 0.74-0.77 at M=2 and 4 per CU), 4 per CU above (12 x f16 0.78,
-// 24 x bf16 0.73).  FP8 inputs keep M=1 and 6 per CU.
+// 24 x bf16 0.73).  FP8 inputs keep M=1, at 12 workgroups per CU for E4M3B15
+// (its decode checks each word for exponent-15 codes; 6 and 12 ranks to
+// E4M3B15 0.70 / 0.71, against 0.52 / 0.55 at 6 per CU) and 8 for E4M3FN
+// (0.74 / 0.74, against 0.70 / 0.75).
 // MRR_RSAG_ANY_M and MRR_RSAG_WPC override.
 constexpr int rsag_any_unroll(int tin, int tout) {
   return is_fp8(tin) ? (tout == kF32 ? 4 : tout == kF16 ? 2 : 1) : 1;
 }
 static int rsag_any_multiplier(int) { return 1; }
 static int rsag_any_wg_per_cu(int n, int tin) {
-  if (is_fp8(tin)) return 6;
+  if (is_fp8(tin)) return tin == kFP8FN ? 8 : 12;
   return n <= 4 ? 16 : n <= 8 ? 8 : 4;
 }
 template <int In, int Acc, int Out>

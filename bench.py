@@ -234,6 +234,9 @@ def bench_rsag(args, torch, mrr, synth):
     torch.cuda.synchronize()
 
     compiled = n in (2, 4, 8, 16, 32)
+    if not compiled and tout != t:
+        raise SystemExit("rank counts outside 2/4/8/16/32 run through mrr_allreduce, whose output "
+                         "type is the input type: --out %s is not available at %d ranks" % (tout, n))
 
     rank = args.rank
     if rank >= 0 and (not compiled or rank >= n):
