@@ -541,7 +541,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the N rank buffers live in one MI355X's HBM, "
-              "so --gpus %d is not a configuration this build runs" % args.gpus, file=sys.stderr)
+              "so --gpus %d (more than one GPU) is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
