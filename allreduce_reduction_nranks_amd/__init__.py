@@ -77,6 +77,7 @@ def load_library() -> ctypes.CDLL:
             "mrr_rank_buffer_pitch": ([sz, i], sz),
             "mrr_status_string": ([i], ctypes.c_char_p),
             "mrr_version": ([], i),
+            "mrr_reload_env": ([], None),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -95,6 +96,8 @@ def _ptr(x) -> int:
 
 
 def _ptrs(xs):
+    if xs is None:
+        return None  # the C ABI refuses a null array with MRR_EINVAL
     return (ctypes.c_void_p * len(xs))(*[_ptr(x) for x in xs])
 
 
@@ -106,6 +109,45 @@ def _dt(d) -> int:
     import torch
     return {torch.float32: MRR_F32, torch.float16: MRR_F16, torch.bfloat16: MRR_BF16,
             torch.uint8: MRR_FP8_E4M3B15}[d]
+
+
+_ESIZE = {MRR_F32: 4, MRR_F16: 2, MRR_BF16: 2, MRR_FP8_E4M3B15: 1, MRR_FP8_E4M3FN: 1}
+
+
+def _nbytes(count, dtype) -> int:
+    """Bytes of `count` elements of dtype (0 for AUTO or an unknown id, which
+    the C ABI refuses on its own)."""
+    return max(0, int(count)) * _ESIZE.get(_dt(dtype), 0)
+
+
+def _room(x, nbytes: int, what: str) -> None:
+    """A tensor argument must hold at least nbytes bytes.  Raw addresses
+    (ints) and None pass unchecked: the C ABI validates what it can see."""
+    if x is None or isinstance(x, int):
+        return
+    if x.nbytes < nbytes:
+        raise ValueError("%s holds %d bytes, the call needs %d" % (what, x.nbytes, nbytes))
+
+
+def _rank_ptrs(xs, nranks: int, nbytes: int, what: str):
+    """Host array of device pointers for a per-rank argument.  The C ABI reads
+    `nranks` entries, so a shorter list is refused here rather than letting it
+    read past the array; tensor entries must hold nbytes bytes each."""
+    if xs is None:
+        return None
+    if nranks > 0 and len(xs) < nranks:
+        raise ValueError("%s has %d entries, nranks is %d" % (what, len(xs), nranks))
+    ptrs = []
+    for x in xs:
+        if x is None:
+            ptrs.append(0)
+        elif isinstance(x, int):
+            ptrs.append(x)
+        else:
+            if x.nbytes < nbytes and len(ptrs) < nranks:
+                _room(x, nbytes, "%s[%d]" % (what, len(ptrs)))
+            ptrs.append(x.data_ptr())
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
 
 
 _raw_stream = None
@@ -144,6 +186,11 @@ def mrr_version() -> int:
     return load_library().mrr_version()
 
 
+def mrr_reload_env() -> None:
+    """Makes the library read its MRR_* environment overrides again."""
+    load_library().mrr_reload_env()
+
+
 def mrr_rank_buffer_pitch(bytes_per_rank: int, nranks: int) -> int:
     return load_library().mrr_rank_buffer_pitch(bytes_per_rank, nranks)
 
@@ -166,22 +213,29 @@ def alloc_rank_buffers(nranks: int, count: int, dtype, device=None):
 
 
 def mrr_allreduce_rsag(inputs, outputs, count, dtype, nranks, stream=None) -> int:
-    return load_library().mrr_allreduce_rsag(_ptrs(inputs), _ptrs(outputs), count, _dt(dtype),
-                                             nranks, _stream(stream))
+    nb = _nbytes(count, dtype)
+    return load_library().mrr_allreduce_rsag(_rank_ptrs(inputs, nranks, nb, "inputs"),
+                                             _rank_ptrs(outputs, nranks, nb, "outputs"), count,
+                                             _dt(dtype), nranks, _stream(stream))
 
 
 def mrr_allreduce_rsag_ex(inputs, outputs, count, dtype_in, accum, dtype_out, nranks, rank=-1,
                           stream=None) -> int:
-    return load_library().mrr_allreduce_rsag_ex(_ptrs(inputs), _ptrs(outputs), count,
-                                                _dt(dtype_in), _dt(accum), _dt(dtype_out),
-                                                nranks, rank, _stream(stream))
+    tout = dtype_in if _dt(dtype_out) == MRR_AUTO else dtype_out
+    return load_library().mrr_allreduce_rsag_ex(
+        _rank_ptrs(inputs, nranks, _nbytes(count, dtype_in), "inputs"),
+        _rank_ptrs(outputs, nranks, _nbytes(count, tout), "outputs"), count, _dt(dtype_in),
+        _dt(accum), _dt(dtype_out), nranks, rank, _stream(stream))
 
 
 def mrr_allreduce_rsag_dual(inputs, outputs, outputs2, count, dtype_in, accum, nranks, rank=-1,
                             stream=None) -> int:
-    return load_library().mrr_allreduce_rsag_dual(_ptrs(inputs), _ptrs(outputs), _ptrs(outputs2),
-                                                  count, _dt(dtype_in), _dt(accum), nranks, rank,
-                                                  _stream(stream))
+    nb = _nbytes(count, dtype_in)
+    return load_library().mrr_allreduce_rsag_dual(
+        _rank_ptrs(inputs, nranks, nb, "inputs"),
+        _rank_ptrs(outputs, nranks, _nbytes(count, MRR_F16), "outputs"),
+        _rank_ptrs(outputs2, nranks, nb, "outputs2"), count, _dt(dtype_in), _dt(accum), nranks,
+        rank, _stream(stream))
 
 
 def mrr_packet_scratch_bytes(count, dtype, nranks) -> int:
@@ -194,18 +248,25 @@ def mrr_packet_flag_bytes(nranks) -> int:
 
 def mrr_allreduce_packet(inputs, outputs, scratch, scratch_bytes, flags, count, dtype, accum,
                          nranks, max_spins, dev_err=None, stream=None) -> int:
+    nb = _nbytes(count, dtype)
+    _room(scratch, scratch_bytes, "scratch")
+    _room(flags, 4 * PKT_FLAG_SLOTS * max(0, nranks), "flags")
     return load_library().mrr_allreduce_packet(
-        _ptrs(inputs), _ptrs(outputs), _ptr(scratch), scratch_bytes, _ptr(flags), count,
-        _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), _stream(stream))
+        _rank_ptrs(inputs, nranks, nb, "inputs"), _rank_ptrs(outputs, nranks, nb, "outputs"),
+        _ptr(scratch), scratch_bytes, _ptr(flags), count, _dt(dtype), _dt(accum), nranks,
+        max_spins, _ptr(dev_err), _stream(stream))
 
 
 def mrr_allreduce_packet_ex(inputs, outputs, scratch, scratch_bytes, flags, count, dtype, accum,
                             nranks, max_spins, dev_err=None, blocks_per_rank=0, threads=0,
                             stream=None) -> int:
+    nb = _nbytes(count, dtype)
+    _room(scratch, scratch_bytes, "scratch")
+    _room(flags, 4 * PKT_FLAG_SLOTS * max(0, nranks), "flags")
     return load_library().mrr_allreduce_packet_ex(
-        _ptrs(inputs), _ptrs(outputs), _ptr(scratch), scratch_bytes, _ptr(flags), count,
-        _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), blocks_per_rank, threads,
-        _stream(stream))
+        _rank_ptrs(inputs, nranks, nb, "inputs"), _rank_ptrs(outputs, nranks, nb, "outputs"),
+        _ptr(scratch), scratch_bytes, _ptr(flags), count, _dt(dtype), _dt(accum), nranks,
+        max_spins, _ptr(dev_err), blocks_per_rank, threads, _stream(stream))
 
 
 def mrr_packet_rsag_scratch_bytes(count, dtype, nranks) -> int:
@@ -215,50 +276,74 @@ def mrr_packet_rsag_scratch_bytes(count, dtype, nranks) -> int:
 def mrr_allreduce_packet_rsag(inputs, outputs, scratch, scratch_bytes, flags, count, dtype, accum,
                               nranks, max_spins, dev_err=None, blocks_per_rank=0, threads=0,
                               stream=None) -> int:
+    nb = _nbytes(count, dtype)
+    _room(scratch, scratch_bytes, "scratch")
+    _room(flags, 4 * PKT_FLAG_SLOTS * max(0, nranks), "flags")
     return load_library().mrr_allreduce_packet_rsag(
-        _ptrs(inputs), _ptrs(outputs), _ptr(scratch), scratch_bytes, _ptr(flags), count,
-        _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), blocks_per_rank, threads,
-        _stream(stream))
+        _rank_ptrs(inputs, nranks, nb, "inputs"), _rank_ptrs(outputs, nranks, nb, "outputs"),
+        _ptr(scratch), scratch_bytes, _ptr(flags), count, _dt(dtype), _dt(accum), nranks,
+        max_spins, _ptr(dev_err), blocks_per_rank, threads, _stream(stream))
 
 
 def mrr_allreduce(inputs, outputs, count, dtype, accum, nranks, scratch=None, scratch_bytes=0,
                   flags=None, packet_max_bytes=0, max_spins=0, dev_err=None, stream=None) -> int:
-    return load_library().mrr_allreduce(_ptrs(inputs), _ptrs(outputs), count, _dt(dtype),
-                                        _dt(accum), nranks, _ptr(scratch), scratch_bytes,
-                                        _ptr(flags), packet_max_bytes, max_spins, _ptr(dev_err),
-                                        _stream(stream))
+    nb = _nbytes(count, dtype)
+    _room(scratch, scratch_bytes, "scratch")
+    _room(flags, 4 * PKT_FLAG_SLOTS * max(0, nranks), "flags")
+    return load_library().mrr_allreduce(_rank_ptrs(inputs, nranks, nb, "inputs"),
+                                        _rank_ptrs(outputs, nranks, nb, "outputs"), count,
+                                        _dt(dtype), _dt(accum), nranks, _ptr(scratch),
+                                        scratch_bytes, _ptr(flags), packet_max_bytes, max_spins,
+                                        _ptr(dev_err), _stream(stream))
 
 
 def mrr_packet_reduce(in_pkts, out_pkts, npkts, dtype, accum, nranks, flag_in, flag_out,
                       max_spins, dev_err=None, stream=None) -> int:
-    return load_library().mrr_packet_reduce(_ptrs(in_pkts), _ptr(out_pkts), npkts, _dt(dtype),
-                                            _dt(accum), nranks, flag_in, flag_out, max_spins,
-                                            _ptr(dev_err), _stream(stream))
+    _room(out_pkts, 8 * max(0, int(npkts)), "out_pkts")
+    return load_library().mrr_packet_reduce(_rank_ptrs(in_pkts, nranks, 8 * max(0, int(npkts)),
+                                                       "in_pkts"), _ptr(out_pkts), npkts,
+                                            _dt(dtype), _dt(accum), nranks, flag_in, flag_out,
+                                            max_spins, _ptr(dev_err), _stream(stream))
 
 
 def mrr_pack(src, pkts, nbytes, flag, stream=None) -> int:
+    _room(src, nbytes, "src")
+    _room(pkts, (max(0, int(nbytes)) + 3) // 4 * 8, "pkts")
     return load_library().mrr_pack(_ptr(src), _ptr(pkts), nbytes, flag, _stream(stream))
 
 
 def mrr_unpack(pkts, dst, nbytes, stream=None) -> int:
+    _room(pkts, (max(0, int(nbytes)) + 3) // 4 * 8, "pkts")
+    _room(dst, nbytes, "dst")
     return load_library().mrr_unpack(_ptr(pkts), _ptr(dst), nbytes, _stream(stream))
 
 
+def _codec_room(src, ein, dst, eout, n):
+    _room(src, max(0, int(n)) * ein, "src")
+    _room(dst, max(0, int(n)) * eout, "dst")
+
+
 def mrr_fp8b15_to_f16(src, dst, n, stream=None) -> int:
+    _codec_room(src, 1, dst, 2, n)
     return load_library().mrr_fp8b15_to_f16(_ptr(src), _ptr(dst), n, _stream(stream))
 
 
 def mrr_fp8b15_to_f32(src, dst, n, stream=None) -> int:
+    _codec_room(src, 1, dst, 4, n)
     return load_library().mrr_fp8b15_to_f32(_ptr(src), _ptr(dst), n, _stream(stream))
 
 
 def mrr_f16_to_fp8b15(src, dst, n, stream=None) -> int:
+    _codec_room(src, 2, dst, 1, n)
     return load_library().mrr_f16_to_fp8b15(_ptr(src), _ptr(dst), n, _stream(stream))
 
 
 def mrr_f32_to_fp8b15(src, dst, n, stream=None) -> int:
+    _codec_room(src, 4, dst, 1, n)
     return load_library().mrr_f32_to_fp8b15(_ptr(src), _ptr(dst), n, _stream(stream))
 
 
 def mrr_stream_copy(src, dst, nbytes, stream=None) -> int:
+    _room(src, nbytes, "src")
+    _room(dst, nbytes, "dst")
     return load_library().mrr_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream))

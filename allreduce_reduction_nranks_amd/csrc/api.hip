@@ -1,6 +1,7 @@
 // api.hip -- the libmrr C ABI: argument validation, type resolution and
 // dispatch to the kernel launchers.  Every check that needs no device runs
 // before any HIP call, so a refused call never touches the GPU.
+#include <atomic>
 #include <mutex>
 #include <stdio.h>
 #include <stdlib.h>
@@ -11,13 +12,51 @@
 
 namespace mrr {
 
-static bool log_enabled() {
-  static const bool on = [] {
-    const char* v = getenv("MRR_LOG");
-    return v && v[0] && v[0] != '0';
-  }();
-  return on;
+// ---------------------------------------------------------------------------
+// Environment overrides: read once when the library is loaded, and again by
+// mrr_reload_env().  Kept in atomics so a reload racing with calls on other
+// threads is well defined (each call sees the old or the new value).
+// ---------------------------------------------------------------------------
+namespace {
+struct EnvOverrides {
+  std::atomic<int> log{0};          // MRR_LOG=1: one stderr line per refused call
+  std::atomic<uint32_t> max_grid{0};  // MRR_MAX_GRID=<g>, 0 = unset
+  std::atomic<int> lds_cap{1};      // MRR_LDS_CAP=0 turns the LDS reservation off
+  std::atomic<int> rsag_wpc{0};     // MRR_RSAG_WPC=<w>, 0 = the launch table
+  std::atomic<int> rsag_any_m{0};   // MRR_RSAG_ANY_M=1|2|4, 0 = the launch table
+  std::atomic<int> rsag_small{1};   // MRR_RSAG_SMALL=0 turns the small-call route off
+  std::atomic<int> codec_u{0};      // MRR_CODEC_U=<u>, 0 = the launch table
+  std::atomic<int> codec_wpc{0};    // MRR_CODEC_WPC=<w>, 0 = the launch table
+};
+EnvOverrides g_env;
+
+int env_atoi(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
 }
+
+void read_env() {
+  const char* lg = getenv("MRR_LOG");
+  g_env.log.store(lg && lg[0] && lg[0] != '0', std::memory_order_relaxed);
+  const char* mg = getenv("MRR_MAX_GRID");
+  const long g = mg ? atol(mg) : 0;
+  g_env.max_grid.store(g > 0 && g < (1L << 30) ? (uint32_t)g : 0u, std::memory_order_relaxed);
+  const char* cap = getenv("MRR_LDS_CAP");
+  g_env.lds_cap.store(!(cap && cap[0] == '0' && cap[1] == '\0'), std::memory_order_relaxed);
+  g_env.rsag_wpc.store(env_atoi("MRR_RSAG_WPC"), std::memory_order_relaxed);
+  g_env.rsag_any_m.store(env_atoi("MRR_RSAG_ANY_M"), std::memory_order_relaxed);
+  const char* sm = getenv("MRR_RSAG_SMALL");
+  g_env.rsag_small.store(!(sm && sm[0] == '0'), std::memory_order_relaxed);
+  g_env.codec_u.store(env_atoi("MRR_CODEC_U"), std::memory_order_relaxed);
+  g_env.codec_wpc.store(env_atoi("MRR_CODEC_WPC"), std::memory_order_relaxed);
+}
+
+struct EnvAtLoad {
+  EnvAtLoad() { read_env(); }
+} g_env_at_load;
+}  // namespace
+
+static bool log_enabled() { return g_env.log.load(std::memory_order_relaxed) != 0; }
 
 static mrr_status refuse(mrr_status st, const char* fn, const char* why) {
   if (log_enabled()) fprintf(stderr, "libmrr: %s refused (%s): %s\n", fn, mrr_status_string(st), why);
@@ -123,34 +162,50 @@ size_t occupancy_lds_bytes(int wpc) {
 }
 
 // MRR_MAX_GRID=<g> limits the one-workgroup-per-tile launches (RS/AG and
-// codec) to g workgroups, each then walking several tiles; read at every call
-// so that a test can exercise that path at small sizes.  0 when unset.
-uint32_t max_grid_override() {
-  const char* v = getenv("MRR_MAX_GRID");
-  if (!v) return 0;
-  const long g = atol(v);
-  return g > 0 && g < (1L << 30) ? (uint32_t)g : 0;
-}
+// codec) to g workgroups, each then walking several tiles, so that a test can
+// exercise that path at small sizes.  0 when unset.
+uint32_t max_grid_override() { return g_env.max_grid.load(std::memory_order_relaxed); }
 
-// MRR_LDS_CAP=0 (read at every call) turns the LDS reservation off: the
-// RS/AG and codec launches then use a persistent grid of wpc workgroups per
-// CU striding over the tiles, which leaves the LDS free for kernels running
-// concurrently on other streams, at 9-17 % lower bandwidth (measured on
-// MI355X: 8 x 64 MiB f16 0.73 of the HBM peak against 0.81, 8 x 256 MiB
-// bf16 0.65 against 0.78, the f16 decode 0.69 against 0.76).
-bool lds_cap_enabled() {
-  const char* v = getenv("MRR_LDS_CAP");
-  return !(v && v[0] == '0' && v[1] == '\0');
-}
+// MRR_LDS_CAP=0 turns the LDS reservation off: the RS/AG and codec launches
+// then use a persistent grid of wpc workgroups per CU striding over the
+// tiles, which leaves the LDS free for kernels running concurrently on other
+// streams, at 9-17 % lower bandwidth (measured on MI355X: 8 x 64 MiB f16 0.73
+// of the HBM peak against 0.81, 8 x 256 MiB bf16 0.65 against 0.78, the f16
+// decode 0.69 against 0.76).
+bool lds_cap_enabled() { return g_env.lds_cap.load(std::memory_order_relaxed) != 0; }
 
-// Workgroups of `kernel` at `threads` threads that fit on the device at once.
+int rsag_wpc_override() { return g_env.rsag_wpc.load(std::memory_order_relaxed); }
+int rsag_any_m_override() { return g_env.rsag_any_m.load(std::memory_order_relaxed); }
+bool rsag_small_enabled() { return g_env.rsag_small.load(std::memory_order_relaxed) != 0; }
+int codec_u_override() { return g_env.codec_u.load(std::memory_order_relaxed); }
+int codec_wpc_override() { return g_env.codec_wpc.load(std::memory_order_relaxed); }
+
+// Workgroups of `kernel` at `threads` threads that fit on the device at once,
+// cached per (kernel, threads, device): the occupancy query costs
+// microseconds and its answer never changes within a process.
 static int max_resident_blocks(const void* kernel, int threads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  struct Entry {
+    const void* kernel;
+    int threads, device, blocks;
+  };
+  static std::mutex mu;
+  static Entry cache[256];
+  static int used = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].kernel == kernel && cache[i].threads == threads && cache[i].device == dev)
+        return cache[i].blocks;
+  }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
     return 0;
-  return per_cu * device_cu_count(dev);
+  const int blocks = per_cu * device_cu_count(dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 256 && blocks > 0) cache[used++] = Entry{kernel, threads, dev, blocks};
+  return blocks;
 }
 
 }  // namespace mrr
@@ -179,7 +234,9 @@ const char* mrr_status_string(mrr_status s) {
   return "unknown mrr_status";
 }
 
-int mrr_version(void) { return 10000; }
+int mrr_version(void) { return 10100; }
+
+void mrr_reload_env(void) { read_env(); }
 
 size_t mrr_rank_buffer_pitch(size_t bytes_per_rank, int nranks) {
   if (bytes_per_rank == 0 || nranks < 1) return 0;
@@ -371,6 +428,7 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   a.max_spins = max_spins;
   return hip_status(launch_packet_allpair(a, nranks, t, tacc, T, batch, (hipStream_t)stream), fn);
 }
+
 
 // Payload words per full chunk of the two-phase packet allreduce: the RS/AG
 // chunk C = roundup(ceil(count / N), 16 / e) elements, C * e / 4 words.

@@ -130,8 +130,8 @@ static void launch_vec_u(dim3 grid, size_t lds, const void* in, void* out, uint6
 template <int Dir>
 static hipError_t launch_codec_dir(const void* in, void* out, uint64_t n, bool vector,
                                    hipStream_t stream) {
-  static const int u_env = [] { const char* v = getenv("MRR_CODEC_U"); return v ? atoi(v) : 0; }();
-  static const int wpc_env = [] { const char* v = getenv("MRR_CODEC_WPC"); return v ? atoi(v) : 0; }();
+  const int u_env = codec_u_override();
+  const int wpc_env = codec_wpc_override();
   const int U = (u_env == 1 || u_env == 2 || u_env == 4 || u_env == 8) ? u_env : codec_unroll(Dir);
   const uint64_t wpc = wpc_env > 0 ? (uint64_t)wpc_env : (uint64_t)codec_wg_per_cu(Dir);
   const uint64_t units = n / CodecShape<Dir>::V;

@@ -134,9 +134,17 @@ int device_cu_count(int device);
 void device_lds_limits(size_t* per_cu, size_t* per_block);
 // Dynamic LDS per workgroup that caps residency at `wpc` workgroups per CU.
 size_t occupancy_lds_bytes(int wpc);
-// MRR_MAX_GRID (read at every call), 0 when unset.
+// Environment overrides (read when the library loads and by mrr_reload_env()).
+// MRR_MAX_GRID, 0 when unset.
 uint32_t max_grid_override();
-// False when MRR_LDS_CAP=0 (read at every call): persistent grids, no LDS reservation.
+// False when MRR_LDS_CAP=0: persistent grids, no LDS reservation.
 bool lds_cap_enabled();
+// MRR_RSAG_WPC, MRR_RSAG_ANY_M, MRR_CODEC_U, MRR_CODEC_WPC: 0 when unset.
+int rsag_wpc_override();
+int rsag_any_m_override();
+int codec_u_override();
+int codec_wpc_override();
+// False when MRR_RSAG_SMALL=0.
+bool rsag_small_enabled();
 
 }  // namespace mrr

@@ -3,8 +3,8 @@
 // Operation ("Support 2 ranks in AllreduceRsAgZeroCopy", MSCCL++ PR #948,
 // sections "why" and "what changed"): rank r reads chunk r of every rank's
 // input, reduces it, and writes the reduced chunk into every rank's output.
-// The kernel is generic in NRanks (NPeers = NRanks - 1) with the rank loops
-// unrolled at compile time, and exists for 2, 4, 8, 16 and 32 ranks.
+// One kernel instance is compiled per rank count (2, 4, 8, 16 and 32), each
+// with its loops over the ranks fully unrolled.
 //
 // MI355X mapping.  All N rank buffers live in this GPU's HBM, so one launch
 // performs every rank's share (or one chosen rank's share).  The work is
@@ -394,10 +394,7 @@ struct RsagShape {
 constexpr uint32_t kMaxGrid = 1u << 24;
 
 static RsagShape rsag_shape(int wpc, uint32_t launch_tiles) {
-  static const int wpc_env = [] {
-    const char* v = getenv("MRR_RSAG_WPC");
-    return v ? atoi(v) : 0;
-  }();
+  const int wpc_env = rsag_wpc_override();
   if (wpc_env > 0) wpc = wpc_env;
   RsagShape sh;
   const bool capped = lds_cap_enabled();
@@ -539,10 +536,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     // Only while its ranks fit one load group (N <= 8): at N = 16 the split
     // into two dependent groups costs more than it gains (3.14 -> 3.44 us).
     // MRR_RSAG_SMALL=0 disables.
-    static const bool small_ok = [] {
-      const char* v = getenv("MRR_RSAG_SMALL");
-      return !(v && v[0] == '0');
-    }();
+    const bool small_ok = rsag_small_enabled();
     bool small = false;
     if (valid_nranks(n) && n <= kAnyGroup && small_ok &&
         rsag_unroll(n, In, Out) > rsag_any_unroll(In, Out))
@@ -550,10 +544,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     const bool any_n = !valid_nranks(n) || small;
     int mult = 1;
     if (any_n && !small && !is_fp8(In) && n <= kAnyGroup) {  // the wide-group kernel runs M = 1
-      static const int m_env = [] {
-        const char* v = getenv("MRR_RSAG_ANY_M");
-        return v ? atoi(v) : 0;
-      }();
+      const int m_env = rsag_any_m_override();
       mult = (m_env == 1 || m_env == 2 || m_env == 4) ? m_env : rsag_any_multiplier(n);
     }
     if (any_n)

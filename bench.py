@@ -85,10 +85,15 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def run(self, fn, steps, warmup):
+    def run(self, fn, steps, warmup, prime=None):
+        """prime(), when given, runs after the warm-up and before the timed
+        region (the benchmark poisons the outputs there, so the parity check
+        afterwards sees what the timed calls wrote)."""
         torch = self.torch
         for _ in range(warmup):
             fn()
+        if prime is not None:
+            prime()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -104,11 +109,12 @@ class Timer:
         kern_ms = e0.elapsed_time(e1) / steps
         return wall_ms, kern_ms
 
-    def run_graph(self, fn, steps, warmup):
+    def run_graph(self, fn, steps, warmup, prime=None):
         """The K calls captured once into a HIP graph and replayed: per-call
         GPU time without the host's per-call launch cost (what a captured
         inference step sees).  The library's calls allocate nothing and keep
-        their state on the device, so replays are valid calls."""
+        their state on the device, so replays are valid calls.  prime() as
+        for run(), before the timed replay."""
         torch = self.torch
         for _ in range(warmup):
             fn()
@@ -122,6 +128,8 @@ class Timer:
                     fn()
         torch.cuda.synchronize()
         g.replay()  # warm replay
+        if prime is not None:
+            prime()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -174,22 +182,155 @@ def add_ceilings(result, ceilings, achieved):
     result["config"]["frac_of_stream_copy"] = round(achieved / stream_gbps, 4)
 
 
-def cpu_baseline_rsag(ins_dev, t, acc, tout, sample_elems):
-    """The oracle, as it stands, on the first sample_elems elements of every
-    rank (single thread)."""
+POISON = 0x5A  # byte written over every output before the timed region
+
+
+def poison(bufs):
+    """Overwrites every output with a byte pattern (outside the timed region),
+    so outputs the timed calls did not write fail the parity check."""
+    for b in bufs:
+        b.view(-1).view(__import__("torch").uint8).fill_(POISON)
+
+
+def host_threads() -> int:
+    """Threads for the oracle's all-cores leg: the CPUs this process may run
+    on, capped by OMP_NUM_THREADS when it is set (a host's share per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def split_range(lo, hi, parts, align=4096):
+    """[lo, hi) as at most `parts` disjoint blocks whose inner edges are
+    multiples of `align` elements."""
+    step = -(-(hi - lo) // max(1, parts))
+    step = max(align, -(-step // align) * align)
+    return [(a, min(hi, a + step)) for a in range(lo, hi, step)]
+
+
+def run_blocks(fn, lo, hi, threads):
+    """fn(a, b) over disjoint blocks of [lo, hi), one block per thread.  The
+    oracle's ctypes calls release the GIL, so the blocks run in parallel; each
+    element is still summed in rank order, so results are those of one call."""
+    blocks = split_range(lo, hi, threads)
+    if threads <= 1 or len(blocks) <= 1:
+        for a, b in blocks:
+            fn(a, b)
+        return
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(blocks)) as ex:
+        for f in [ex.submit(fn, a, b) for a, b in blocks]:
+            f.result()
+
+
+def oracle_legs(block_fn, elems_total, bytes_per_elem, sample_bytes, threads, what):
+    """The CPU baseline: the oracle as it stands timed on one thread and on
+    `threads` threads (disjoint element blocks), each over a bounded prefix of
+    the workload -- sample_bytes of algorithmic bytes per thread -- with one
+    warm-up run and the median of three timed runs.  block_fn(a, b) runs the
+    oracle over elements [a, b) of every rank."""
+    import statistics
+    legs = []
+    for th in (1, threads):
+        elems = min(elems_total, max(4096, th * sample_bytes // bytes_per_elem))
+        runs = []
+        for i in range(4):  # 1 warm-up + 3 timed
+            t0 = time.perf_counter()
+            run_blocks(block_fn, 0, elems, th)
+            if i:
+                runs.append(time.perf_counter() - t0)
+        med = statistics.median(runs)
+        legs.append({"threads": th, "value": round(elems * bytes_per_elem / med / 1e9, 4),
+                     "unit": "GB/s", "median_s": round(med, 3),
+                     "runs_s": [round(r, 3) for r in runs], "elements_per_rank": elems,
+                     "fraction_of_workload": round(elems / elems_total, 4)})
+        if threads == 1:
+            break
+    best = legs[-1]
+    return {"value": best["value"], "unit": "GB/s", "cores": best["threads"], "kind": "oracle",
+            "host_cores": os.cpu_count(), "threads_available": threads,
+            "sample": "%s; first %d elements of every rank (%.1f%% of the workload) on %d "
+                      "threads, and the first %d on one thread; 1 warm-up + median of 3 runs "
+                      "each" % (what, best["elements_per_rank"],
+                                100.0 * best["fraction_of_workload"], best["threads"],
+                                legs[0]["elements_per_rank"]),
+            "legs": legs}
+
+
+_NAN_TEST = {  # bit pattern -> NaN, on integer views of the element type
+    "f32": lambda x: (x & 0x7FFFFFFF) > 0x7F800000,
+    "f16": lambda x: (x & 0x7FFF) > 0x7C00,
+    "bf16": lambda x: (x & 0x7FFF) > 0x7F80,
+    "fp8": lambda x: (x & 0x7F) > 0x78,
+    "fp8fn": lambda x: (x & 0x7F) == 0x7F,
+}
+
+
+def count_mismatches(torch, outs, want_bits, t, lo=0):
+    """Elements of outs[k][lo : lo + len(want_bits)] whose bits differ from
+    the oracle's (NaN against NaN counts as equal: only NaN-ness is
+    specified), summed over every output k; compared on the GPU."""
+    import numpy as np
+    e = ESIZE[t]
+    ints = {1: (np.uint8, torch.uint8), 2: (np.int16, torch.int16), 4: (np.int32, torch.int32)}[e]
+    want = torch.from_numpy(np.ascontiguousarray(want_bits).view(ints[0])).to("cuda")
+    n = want.numel()
+    bad = 0
+    for o in outs:
+        got = o.view(-1).view(torch.uint8)[lo * e:(lo + n) * e].view(ints[1])
+        diff = got != want
+        if bool(diff.any()):
+            isnan = _NAN_TEST[t]
+            diff &= ~(isnan(got) & isnan(want))
+            bad += int(diff.sum())
+    return bad
+
+
+def verify_rsag(torch, orc, host_ins, outs, t, acc, tout, lo, hi, threads):
+    """The oracle over elements [lo, hi) of every rank (all host threads, on
+    disjoint blocks), compared with every output of the last timed call."""
+    import numpy as np
+    NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8,
+          "fp8fn": np.uint8}
+    want = np.empty(hi - lo, dtype=NP[tout])
+
+    def block(a, b):
+        orc.allreduce([x[a:b] for x in host_ins], t, acc, tout, out=want[a - lo:b - lo])
+
+    t0 = time.perf_counter()
+    run_blocks(block, lo, hi, threads)
+    dt = time.perf_counter() - t0
+    bad = count_mismatches(torch, outs, want, tout, lo)
+    return {"mismatches": bad, "elements": len(outs) * (hi - lo), "outputs": len(outs),
+            "oracle_s": round(dt, 2), "threads": threads,
+            "checked": "every element of every output of the last timed call, bit for bit "
+                       "against the oracle (outputs poisoned before the timed region)"}
+
+
+def cpu_baseline_rsag(args, torch, ins_dev, outs, t, acc, tout, lo, hi):
+    """The cpu_baseline leg: the oracle timed on this host (one thread and all
+    threads), then run over the whole measured range to check the timed
+    call's outputs."""
     import oracle
     import synth
-    n = len(ins_dev)
-    sub = [synth.to_bits_numpy(x[:sample_elems]) for x in ins_dev]
-    oracle.default()  # build/load outside the timed region
-    t0 = time.perf_counter()
-    oracle.allreduce_all(sub, t, acc, tout)
-    dt = time.perf_counter() - t0
-    nbytes = n * sample_elems * (ESIZE[t] + ESIZE[tout])
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "first %d elements of each of the %d ranks (%.1f%% of the workload), "
-                      "all %d outputs written, one thread, %.1f s"
-                      % (sample_elems, n, 100.0 * sample_elems / ins_dev[0].numel(), n, dt)}
+    orc = oracle.default()  # build/load outside the timed runs
+    threads = host_threads()
+    host_ins = [synth.to_bits_numpy(x) for x in ins_dev]
+    n = len(host_ins)
+    per_elem = n * (ESIZE[t] + ESIZE[tout])
+
+    def block(a, b):
+        orc.allreduce_all([x[a:b] for x in host_ins], t, acc, tout)
+
+    base = oracle_legs(block, host_ins[0].size, per_elem, args.cpu_sample_mib * MiB, threads,
+                       "all %d outputs written" % n)
+    parity = verify_rsag(torch, orc, host_ins, outs, t, acc, tout, lo, hi, threads)
+    return base, parity
 
 
 def bench_rsag(args, torch, mrr, synth):
@@ -251,20 +392,25 @@ def bench_rsag(args, torch, mrr, synth):
             raise mrr.MrrError(st)
 
     if rank < 0:
-        alg_bytes = n * count * (ESIZE[t] + ESIZE[tout])
+        lo, hi = 0, count
     else:  # one rank's share: chunk `rank` of every input, written to every output
         gran = 256 // ESIZE[t]  # chunk widths are rounded to 256 bytes of input
         per = -(-count // n)
         chunk = -(-per // gran) * gran
-        elems = max(0, min(count, (rank + 1) * chunk) - min(count, rank * chunk))
-        alg_bytes = n * elems * (ESIZE[t] + ESIZE[tout])
+        lo, hi = min(count, rank * chunk), min(count, (rank + 1) * chunk)
+    alg_bytes = n * (hi - lo) * (ESIZE[t] + ESIZE[tout])
     graph = use_graph(args, alg_bytes)
     eager_us = None
+    prime = lambda: poison(outs)  # noqa: E731
     if graph:
         eager_us = Timer(torch).run(step, args.steps, args.warmup)[1] * 1e3
-        wall_ms, kern_ms = Timer(torch).run_graph(step, args.steps, args.warmup)
+        wall_ms, kern_ms = Timer(torch).run_graph(step, args.steps, args.warmup, prime)
     else:
-        wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+        wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup, prime)
+    # Nothing below writes `outs` again (the layout comparison and the copy
+    # ceiling use buffers of their own): the parity check reads what the last
+    # timed call wrote.
+    checked = outs
     sep_us = None
     if args.layout == "pitch" and args.layout_compare:
         def step_sep():
@@ -312,15 +458,16 @@ def bench_rsag(args, torch, mrr, synth):
         result["config"]["eager_us_per_call"] = round(eager_us, 2)
     if rank >= 0:
         # One rank's share (the per-GPU work of the sharded layout); the
-        # counter summaries and the oracle baseline cover whole calls only.
+        # counter summaries cover whole calls only.
         result["config"]["workload"] += (", rank %d's share only (chunk %d of every input, "
                                          "written to all %d outputs)" % (rank, rank, n))
         result["config"]["rank"] = rank
         result["roofline"]["traffic"] = None
-        return result
     if args.cpu_baseline:
-        sample = min(count, args.cpu_sample)
-        result["cpu_baseline"] = cpu_baseline_rsag(ins, t, acc, tout, sample)
+        base, parity = cpu_baseline_rsag(args, torch, ins, checked, t, acc, tout, lo, hi)
+        if rank < 0:
+            result["cpu_baseline"] = base
+        result["parity"] = parity
     return result
 
 
@@ -346,11 +493,12 @@ def bench_packet(args, torch, mrr, synth):
     S = count * 2
     graph = use_graph(args, 3 * n * S + 4 * n * (n - 1) * S)
     eager_us = None
+    prime = lambda: poison(outs)  # noqa: E731
     if graph:
         eager_us = Timer(torch).run(step, args.steps, args.warmup)[1] * 1e3
-        wall_ms, kern_ms = Timer(torch).run_graph(step, args.steps, args.warmup)
+        wall_ms, kern_ms = Timer(torch).run_graph(step, args.steps, args.warmup, prime)
     else:
-        wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+        wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup, prime)
     if int(err.item()) != 0:
         raise RuntimeError("packet poll timed out")
     # allpair: send reads NS, packets 2N(N-1)S written and read, own input NS, outputs NS.
@@ -358,7 +506,7 @@ def bench_packet(args, torch, mrr, synth):
     # ag packets 2(N-1)S written and read.
     alg_bytes = (3 * n * S + 8 * (n - 1) * S) if two_phase else (3 * n * S + 4 * n * (n - 1) * S)
     name = "two-phase (RS + AG) packet" if two_phase else "LL-packet allpair"
-    return {
+    result = {
         "metric": "%s allreduce latency" % name, "value": round(kern_ms * 1e3, 3),
         "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall_ms, 5), "higher_is_better": False, "scaling": "weak",
@@ -370,6 +518,12 @@ def bench_packet(args, torch, mrr, synth):
                    "timing": TIMING_GRAPH if graph else TIMING_EAGER,
                    "eager_us_per_call": None if eager_us is None else round(eager_us, 3)},
     }
+    if args.cpu_baseline:
+        base, parity = cpu_baseline_rsag(args, torch, ins, outs, t, "f32", t, 0, count)
+        base["sample"] += " (the RS/AG sum the packet path must equal)"
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+    return result
 
 
 def bench_dual(args, torch, mrr, synth):
@@ -394,7 +548,8 @@ def bench_dual(args, torch, mrr, synth):
         if st != mrr.MRR_OK:
             raise mrr.MrrError(st)
 
-    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup,
+                                        lambda: poison(list(o16) + list(o8)))
     alg_bytes = n * count * (1 + 2 + 1)
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
@@ -421,18 +576,24 @@ def bench_dual(args, torch, mrr, synth):
         add_ceilings(result, copy_ceiling(torch, mrr, n * count), achieved)
     if args.cpu_baseline:
         import oracle
-        sample = min(count, args.cpu_sample)
-        sub = [synth.to_bits_numpy(x[:sample]) for x in ins]
-        oracle.default()
-        t0 = time.perf_counter()
-        oracle.allreduce_all(sub, t, acc, "f16")
-        oracle.allreduce_all(sub, t, acc, t)
-        dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {
-            "value": round(n * sample * 4 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "first %d elements of each of the %d ranks (%.1f%% of the workload), both "
-                      "output sets written, one thread, %.1f s" % (sample, n, 100.0 * sample / count, dt)}
+        orc = oracle.default()
+        threads = host_threads()
+        host_ins = [synth.to_bits_numpy(x) for x in ins]
+
+        def block(a, b):
+            sub = [x[a:b] for x in host_ins]
+            orc.allreduce_all(sub, t, acc, "f16")
+            orc.allreduce_all(sub, t, acc, t)
+
+        result["cpu_baseline"] = oracle_legs(block, count, n * 4, args.cpu_sample_mib * MiB,
+                                             threads, "both output sets written")
+        p16 = verify_rsag(torch, orc, host_ins, o16, t, acc, "f16", 0, count, threads)
+        p8 = verify_rsag(torch, orc, host_ins, o8, t, acc, t, 0, count, threads)
+        result["parity"] = {"mismatches": p16["mismatches"] + p8["mismatches"],
+                            "elements": p16["elements"] + p8["elements"],
+                            "outputs": p16["outputs"] + p8["outputs"],
+                            "oracle_s": round(p16["oracle_s"] + p8["oracle_s"], 2),
+                            "threads": threads, "checked": p16["checked"] + ", both output sets"}
     return result
 
 
@@ -461,7 +622,7 @@ def bench_codec(args, torch, mrr, synth):
         if st != mrr.MRR_OK:
             raise mrr.MrrError(st)
 
-    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup)
+    wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup, lambda: poison([dst]))
     alg_bytes = n * (ESIZE[tin] + ESIZE[tout])
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
@@ -484,18 +645,34 @@ def bench_codec(args, torch, mrr, synth):
     }
     add_ceilings(result, ceiling, achieved)
     if args.cpu_baseline:
+        import numpy as np
         import oracle
-        sample = min(n, args.cpu_sample)
-        host = synth.to_bits_numpy(src[:sample])
-        oracle.default()
+        orc = oracle.default()
+        threads = host_threads()
+        host = synth.to_bits_numpy(src)
+
+        def block(a, b):
+            orc.convert(host[a:b], tin, tout)
+
+        result["cpu_baseline"] = oracle_legs(block, n, ESIZE[tin] + ESIZE[tout],
+                                             args.cpu_sample_mib * MiB, threads, "conversion")
+        NP = {"f32": np.float32, "f16": np.uint16, "fp8": np.uint8}
+        want = np.empty(n, dtype=NP[tout])
+
+        def full(a, b):
+            orc.convert(host[a:b], tin, tout, out=want[a:b])
+
         t0 = time.perf_counter()
-        oracle.convert(host, tin, tout)
+        run_blocks(full, 0, n, threads)
         dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {
-            "value": round(sample * (ESIZE[tin] + ESIZE[tout]) / dt / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": "first %d elements (%.1f%% of the workload), one thread, %.1f s"
-                      % (sample, 100.0 * sample / n, dt)}
+        out_t = {"f32": "f32", "f16": "f16", "fp8": "fp8"}[tout]
+        result["parity"] = {"mismatches": count_mismatches(torch, [dst.view(torch.uint8)], want,
+                                                           out_t),
+                            "elements": n, "outputs": 1, "oracle_s": round(dt, 2),
+                            "threads": threads,
+                            "checked": "every element of the last timed call's output, bit for "
+                                       "bit against the oracle (output poisoned before the "
+                                       "timed region)"}
     return result
 
 
@@ -524,8 +701,10 @@ def main():
     ap.add_argument("--layout", default="pitch", choices=["pitch", "separate"],
                     help="rank buffer placement: one allocation per side at mrr_rank_buffer_pitch() "
                          "spacing (default), or one allocation per buffer")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 30,
-                    help="elements per rank the CPU oracle baseline reduces")
+    ap.add_argument("--cpu-sample-mib", type=int, default=128,
+                    help="CPU baseline: algorithmic MiB per thread in each timed oracle run "
+                         "(the one-thread and all-threads legs each cover a prefix of the "
+                         "workload of that many MiB per thread)")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-copy-ceiling", dest="copy_ceiling", action="store_false")
     ap.add_argument("--layout-compare", action="store_true",
@@ -560,6 +739,11 @@ def main():
     else:
         result = bench_rsag(args, torch, mrr, synth)
     print(json.dumps(result), flush=True)
+    parity = result.get("parity")
+    if parity is not None and parity["mismatches"] != 0:
+        print("bench.py: %d of %d output elements differ from the oracle"
+              % (parity["mismatches"], parity["elements"]), file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -8,9 +8,9 @@
  *   - RS/AG zero-copy allreduce: "Support 2 ranks in AllreduceRsAgZeroCopy"
  *     (MSCCL++ PR #948), sections "why" and "what changed": rank r reduces
  *     chunk r of every rank's input and writes the result straight into every
- *     rank's output, with no scratch; the kernel is generic in NRanks
- *     (NPeers = NRanks - 1, peer loops unrolled at compile time) and exists
- *     for 2, 4, 8, 16 and 32 ranks; any other rank count is refused.
+ *     rank's output, with no scratch; it is compiled once per rank count,
+ *     with the rank loops unrolled, for 2, 4, 8, 16 and 32 ranks; any other
+ *     rank count is refused.
  *   - LL-packet allpair allreduce: MSCCL++ commit history (/src), entry fixing
  *     the allreduce_allpair_packet algorithm: packets go to a scratch area so
  *     the input is never overwritten, one workgroup sends, reduces and writes
@@ -38,7 +38,7 @@
  *     caches only per-device properties (CU count, occupancy).
  *   - Validation happens before any launch: on an error nothing is launched
  *     and the specific status is returned.  MRR_LOG=1 in the environment
- *     prints one stderr line per refused call.
+ *     prints one stderr line per refused call (see mrr_reload_env).
  *   - count == 0 (or n == 0) returns MRR_OK without launching.
  *   - Element types travel as raw bits: f16 / bf16 as 16-bit IEEE binary16 /
  *     bfloat16, FP8 E4M3B15 as one byte (sign, 4-bit exponent with bias 15,
@@ -193,6 +193,13 @@ mrr_status mrr_allreduce_rsag_dual(const void* const* inputs, void* const* outpu
  *           algorithm may change between calls without a hang, and graph
  *           replays advance F on the device.  All ranks' slots must hold the
  *           same value.  May be shared with later calls of any packet entry.
+ *           Flag wrap: after 2^32 - 1 calls on one flag buffer F returns to
+ *           1.  Scratch packets that an earlier, larger call wrote and no
+ *           later call rewrote keep their old flags, which the wrapped
+ *           sequence reaches again, and a poll could then take such a stale
+ *           packet for a new one.  Re-zero the flags and the scratch together
+ *           before 2^32 - 1 calls (about 2.4 hours of back-to-back 2 us
+ *           calls).
  * inputs / outputs: device, 4-byte aligned (MRR_EALIGN), outputs[k] may be
  *           inputs[k] exactly; other overlaps give MRR_EOVERLAP.
  * dtype:    F32 | F16 | BF16 | FP8_E4M3B15 (output type == input type).
@@ -345,6 +352,21 @@ mrr_status mrr_stream_copy(const void* src, void* dst, size_t nbytes, void* stre
  * bytes == 0 or nranks < 1.
  * ------------------------------------------------------------------------ */
 size_t mrr_rank_buffer_pitch(size_t bytes_per_rank, int nranks);
+
+/* --------------------------------------------------------------------------
+ * Environment overrides (diagnostics and tuning; none changes a result).
+ *   MRR_LOG=1          one stderr line per refused call
+ *   MRR_MAX_GRID=<g>   at most g workgroups per RS/AG, codec or copy launch
+ *                      (each then walks several tiles)
+ *   MRR_LDS_CAP=0      persistent grids without the LDS reservation that caps
+ *                      residency (frees the LDS for concurrent kernels)
+ *   MRR_RSAG_WPC, MRR_RSAG_ANY_M, MRR_RSAG_SMALL=0, MRR_CODEC_U, MRR_CODEC_WPC
+ *                      replace entries of the measured launch tables
+ * They are read once, when the library is loaded.  mrr_reload_env() reads
+ * them again (for tests and tuning sweeps that change them in-process); calls
+ * running on other threads meanwhile see either the old or the new values.
+ * ------------------------------------------------------------------------ */
+void mrr_reload_env(void);
 
 /* Static description of a status code (never NULL). */
 const char* mrr_status_string(mrr_status status);

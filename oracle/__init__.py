@@ -73,6 +73,9 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_allreduce_packet_rsag.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz,
                                             i, i, i, u32]
     L.orc_allreduce_packet_rsag.restype = i
+    L.orc_allreduce_fullmesh.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, i, i, i,
+                                         i, u32]
+    L.orc_allreduce_fullmesh.restype = i
     return L
 
 
@@ -114,17 +117,24 @@ class Oracle:
     def __init__(self, L: ctypes.CDLL):
         self.L = L
 
-    def allreduce(self, inputs, t_in: str, accum: str = "f32", t_out: str | None = None) -> np.ndarray:
+    def allreduce(self, inputs, t_in: str, accum: str = "f32", t_out: str | None = None,
+                  out: np.ndarray | None = None) -> np.ndarray:
         """Elementwise sum over ranks in order 0..N-1 (the RS/AG result).
 
         Returns ONE output array: by definition all N outputs are this array.
+        `out`, when given, is a contiguous array of count elements of the
+        output type's bits that receives the result (and is returned).
         """
         t_out = t_out or t_in
         accum = _accum(t_in, accum)
         ins = [_bits(a, t_in) for a in inputs]
         count = ins[0].size
         assert all(a.size == count for a in ins)
-        out = np.empty(count, dtype=NP_BITS[t_out])
+        if out is None:
+            out = np.empty(count, dtype=NP_BITS[t_out])
+        else:
+            assert out.flags.c_contiguous and out.size == count
+            assert out.dtype == np.dtype(NP_BITS[t_out])
         rc = self.L.orc_allreduce(_ptr_array(ins), _ptr_array([out]), count, TYPE_IDS[t_in],
                                  TYPE_IDS[accum], TYPE_IDS[t_out], len(ins), 1)
         if rc != 0:
@@ -144,10 +154,15 @@ class Oracle:
             raise ValueError("oracle rejected types")
         return outs
 
-    def convert(self, a, t_in: str, t_out: str) -> np.ndarray:
-        """Elementwise conversion: exact decode, one RNE rounding (FP8 saturates)."""
+    def convert(self, a, t_in: str, t_out: str, out: np.ndarray | None = None) -> np.ndarray:
+        """Elementwise conversion: exact decode, one RNE rounding (FP8 saturates).
+        `out` as for allreduce()."""
         a = _bits(a, t_in)
-        out = np.empty(a.size, dtype=NP_BITS[t_out])
+        if out is None:
+            out = np.empty(a.size, dtype=NP_BITS[t_out])
+        else:
+            assert out.flags.c_contiguous and out.size == a.size
+            assert out.dtype == np.dtype(NP_BITS[t_out])
         if self.L.orc_convert(_ptr(a), _ptr(out), a.size, TYPE_IDS[t_in], TYPE_IDS[t_out]) != 0:
             raise ValueError("bad types")
         return out
@@ -223,6 +238,36 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected types")
         return scratch[0], scratch[1], outs[0]
+
+    @staticmethod
+    def fullmesh_layout(count: int, t: str, nranks: int):
+        """(chunk elements C, semaphore bytes, inbox bytes) of the full-mesh
+        scratch image: N*N*1024 uint64 semaphores, then N*N*C*e inbox bytes."""
+        e = ELEM_SIZE[t]
+        per = -(-count // nranks)
+        chunk = -(-per // (16 // e)) * (16 // e)
+        return chunk, nranks * nranks * 1024 * 8, nranks * nranks * chunk * e
+
+    def allreduce_fullmesh(self, inputs, t: str, accum: str, flag: int, nblocks: int,
+                           scratch: np.ndarray | None = None):
+        """Expected (scratch image, output) after one full-mesh allreduce with
+        flag F and nblocks blocks per rank, starting from `scratch` (a uint8
+        image of the whole scratch; zeros when None).  The returned image is a
+        new array; see the C source for what the call writes."""
+        accum = _accum(t, accum)
+        ins = [_bits(a, t) for a in inputs]
+        n = len(ins)
+        count = ins[0].size
+        _, sem_b, box_b = self.fullmesh_layout(count, t, n)
+        img = np.zeros(sem_b + box_b, dtype=np.uint8) if scratch is None else \
+            np.array(scratch, dtype=np.uint8, copy=True).ravel()
+        assert img.size >= sem_b + box_b
+        outs = [np.empty(count, dtype=NP_BITS[t]) for _ in ins]
+        rc = self.L.orc_allreduce_fullmesh(_ptr_array(ins), _ptr_array(outs), _ptr(img), count,
+                                           TYPE_IDS[t], TYPE_IDS[accum], n, nblocks, flag)
+        if rc != 0:
+            raise ValueError("oracle rejected arguments")
+        return img, outs[0]
 
     def packet_reduce(self, in_pkts, t: str, accum: str, flag_in: int, flag_out: int):
         """Receive step alone.  Returns the output packets, or None when some input

@@ -450,3 +450,53 @@ int orc_packet_reduce(const uint64_t* const* in_pkts, uint64_t* out_pkts, size_t
   }
   return 0;
 }
+
+/* Full-mesh allreduce (the commit history names a "fullmesh" allreduce beside
+ * the allpair packet one, in the entries adding accumDtype and ROCm FP8
+ * support; its steps are not on the pages, so this follows the plain reading
+ * of the name: every rank exchanges data directly with every peer, by writes
+ * only, in plain data rather than LL packets, with a flag written after the
+ * data to signal it):
+ *   1. rank d writes chunk c of its input into inbox [c][d] of the scratch,
+ *      for every peer c != d;
+ *   2. it then sets, for every peer c != d and block b < nblocks, semaphore
+ *      [c][d][b] to the call's flag F (the flag in the high 32 bits, as in a
+ *      packet, the low 32 bits zero);
+ *   3. rank c, once the semaphores from every peer carry F, sums chunk c in
+ *      rank order (its own chunk from its input, the others from its inbox)
+ *      and writes the result into chunk c of every rank's output.
+ * Chunks as the two-phase packet variant: C = roundup(ceil(count/N), 16/e)
+ * elements, chunk c = elements [c*C, min((c+1)*C, count)).
+ * Expected state after one call with flag F, in a scratch image laid out as
+ *   semaphores: N*N*1024 uint64, [dst][src][slot]
+ *   inboxes:    N*N*C*e bytes, [dst][src][byte of chunk]
+ * the semaphore slots b < nblocks of every pair dst != src hold F << 32, the
+ * inbox bytes of every element of chunk dst below count hold that element of
+ * input src (dst != src), every other byte of the image keeps its previous
+ * value, and every output equals orc_allreduce's. */
+int orc_allreduce_fullmesh(const void* const* inputs, void* const* outputs, uint8_t* scratch,
+                           size_t count, int t, int tacc, int nranks, int nblocks,
+                           uint32_t flag) {
+  build_tables();
+  int e = orc_size(t);
+  if (!e || !orc_size(tacc) || nranks < 1 || nblocks < 1 || nblocks > 1024) return -1;
+  size_t per = (count + (size_t)nranks - 1) / (size_t)nranks;
+  size_t vw = 16 / (size_t)e;
+  size_t chunk = (per + vw - 1) / vw * vw;
+  size_t n = (size_t)nranks;
+  uint64_t* sem = (uint64_t*)scratch;
+  uint8_t* inbox = scratch + n * n * 1024 * sizeof(uint64_t);
+  for (size_t dst = 0; dst < n; ++dst)
+    for (size_t src = 0; src < n; ++src) {
+      if (dst == src) continue;
+      for (int b = 0; b < nblocks; ++b) sem[(dst * n + src) * 1024 + (size_t)b] = (uint64_t)flag << 32;
+      uint8_t* slot = inbox + (dst * n + src) * chunk * (size_t)e;
+      const uint8_t* in = (const uint8_t*)inputs[src];
+      for (size_t j = 0; j < chunk; ++j) {
+        size_t i = dst * chunk + j;
+        if (i >= count) break;
+        memcpy(slot + j * (size_t)e, in + i * (size_t)e, (size_t)e);
+      }
+    }
+  return orc_allreduce(inputs, outputs, count, t, tacc, t, nranks, nranks);
+}

@@ -155,8 +155,8 @@ def test_packet_argument_checks(lib):
 def test_packet_reduce_and_pack_checks(lib):
     ins = [fake(r) for r in range(4)]
     L = mrr
-    assert L.mrr_packet_reduce(ins, fake(100), 64, "f16", "f32", 5, 1, 2, 10, None, 0) \
-        == mrr.MRR_EUNSUPPORTED
+    assert L.mrr_packet_reduce(ins + [fake(4)], fake(100), 64, "f16", "f32", 5, 1, 2, 10, None,
+                               0) == mrr.MRR_EUNSUPPORTED
     assert L.mrr_packet_reduce(ins, fake(100, off=4), 64, "f16", "f32", 4, 1, 2, 10, None, 0) \
         == mrr.MRR_EALIGN
     assert L.mrr_packet_reduce(ins, fake(1, off=64), 64, "f16", "f32", 4, 1, 2, 10, None, 0) \
@@ -304,3 +304,40 @@ def test_packet_size_helpers_refuse_what_the_calls_refuse(lib):
         assert f(1024, "f16", 33) == 0 and f(1024, "f16", 0) == 0
         assert f(1024, "f16", 8) > 0
     assert mrr.mrr_packet_flag_bytes(33) == 0 and mrr.mrr_packet_flag_bytes(32) == 32 * 1024 * 4
+
+
+def test_binding_refuses_short_pointer_lists_and_small_tensors(lib):
+    """The C ABI reads nranks entries of every pointer array: the binding
+    refuses a shorter list before the call, and a tensor smaller than the
+    call's byte count (CPU tensors here; nothing reaches the library)."""
+    import torch
+    ins = [fake(r) for r in range(4)]
+    outs = [fake(64 + r) for r in range(4)]
+    with pytest.raises(ValueError, match="entries"):
+        mrr.mrr_allreduce_rsag(ins[:3], outs, 1024, "f16", 4, stream=0)
+    with pytest.raises(ValueError, match="entries"):
+        mrr.mrr_allreduce_rsag_ex(ins, outs[:2], 1024, "f16", "f32", "f16", 4, -1, stream=0)
+    with pytest.raises(ValueError, match="entries"):
+        mrr.mrr_allreduce(ins[:1], outs, 1024, "f16", "f32", 4, stream=0)
+    with pytest.raises(ValueError, match="entries"):
+        mrr.mrr_allreduce_packet(ins, outs[:3], fake(200), 1 << 20, fake(300), 16, "f16", "f32",
+                                 4, 10, None, 0)
+    with pytest.raises(ValueError, match="entries"):
+        mrr.mrr_packet_reduce(ins[:2], fake(100), 64, "f16", "f32", 4, 1, 2, 10, None, 0)
+    small = [torch.empty(1023, dtype=torch.float16) for _ in range(4)]
+    with pytest.raises(ValueError, match="holds"):
+        mrr.mrr_allreduce_rsag(small, outs, 1024, "f16", 4, stream=0)
+    with pytest.raises(ValueError, match="holds"):  # f32 outputs of FP8 inputs: 4 bytes each
+        mrr.mrr_allreduce_rsag_ex(ins, [torch.empty(1024, dtype=torch.float16)] * 4, 1024,
+                                  "fp8", "f32", "f32", 4, -1, stream=0)
+    with pytest.raises(ValueError, match="holds"):
+        mrr.mrr_fp8b15_to_f32(fake(0), torch.empty(15, dtype=torch.float32), 16, 0)
+    with pytest.raises(ValueError, match="holds"):
+        mrr.mrr_allreduce_packet(ins, outs, torch.empty(8, dtype=torch.int64), 128, fake(300),
+                                 16, "f16", "f32", 4, 10, None, 0)
+    with pytest.raises(ValueError, match="holds"):
+        mrr.mrr_allreduce_packet(ins, outs, fake(200), 1 << 20, torch.zeros(4095, dtype=torch.int32),
+                                 16, "f16", "f32", 4, 10, None, 0)
+    # longer lists are fine: the library reads the first nranks entries
+    assert mrr.mrr_allreduce_rsag(ins + [fake(9)], outs + [fake(99)], 0, "f16", 4, stream=0) \
+        == mrr.MRR_OK

@@ -114,8 +114,8 @@ def test_full_size_32mib_codes():
 
 
 @pytest.mark.parametrize("grid,cap", [(1, "1"), (5, "1"), (0, "0")])
-def test_workgroups_walk_tiles(grid, cap, monkeypatch):
-    """Fewer workgroups than tiles: MRR_MAX_GRID (read per call) caps the
+def test_workgroups_walk_tiles(grid, cap, mrr_env):
+    """Fewer workgroups than tiles: MRR_MAX_GRID (re-read through mrr_reload_env) caps the
     grid, so each workgroup walks several tiles, as calls above 2^22 tiles
     do; MRR_LDS_CAP=0 selects the persistent grid without LDS reservation."""
     announce("codec tile walk", grid, cap)
@@ -125,8 +125,8 @@ def test_workgroups_walk_tiles(grid, cap, monkeypatch):
     f16 = rng.integers(0, 1 << 16, n, dtype=np.uint16)
     f32 = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
     if grid:
-        monkeypatch.setenv("MRR_MAX_GRID", str(grid))
-    monkeypatch.setenv("MRR_LDS_CAP", cap)
+        mrr_env("MRR_MAX_GRID", str(grid))
+    mrr_env("MRR_LDS_CAP", cap)
     c = torch.from_numpy(codes).cuda()
     h = torch.from_numpy(f16.view(np.int16)).cuda()
     f = torch.from_numpy(f32.view(np.int32)).cuda()
@@ -139,8 +139,8 @@ def test_workgroups_walk_tiles(grid, cap, monkeypatch):
     assert mrr.mrr_f16_to_fp8b15(h, e16, n) == mrr.MRR_OK
     assert mrr.mrr_f32_to_fp8b15(f, e32, n) == mrr.MRR_OK
     torch.cuda.synchronize()
-    monkeypatch.delenv("MRR_MAX_GRID", raising=False)
-    monkeypatch.delenv("MRR_LDS_CAP")
+    mrr_env("MRR_MAX_GRID", None)
+    mrr_env("MRR_LDS_CAP", None)
     assert_bits_equal(bits(o16).view(np.uint16), oracle.convert(codes, "fp8", "f16"), "f16", "dec16")
     assert_bits_equal(bits(o32).view(np.uint32), oracle.convert(codes, "fp8", "f32"), "f32", "dec32")
     assert np.array_equal(bits(e16), oracle.convert(f16, "f16", "fp8")), "enc16"

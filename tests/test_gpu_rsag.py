@@ -295,7 +295,7 @@ def test_rank_sweep_256mib_bf16_sampled(n):
 
 # Launches of more tiles than MRR_MAX_GRID workgroups: each workgroup walks
 # several tiles (the path calls above 2^24 tiles take), including partial
-# tiles at chunk ends and the element tail.  The override is read per call.
+# tiles at chunk ends and the element tail (the mrr_env fixture sets the override).
 WALK_CASES = [(2, "bf16", "f32", "bf16"), (8, "f16", "f32", "f16"), (16, "f32", "f32", "f32"),
               (32, "bf16", "f32", "bf16"), (8, "fp8", "f32", "fp8"), (8, "fp8fn", "f32", "f32"),
               (4, "fp8", "f32", "f16")]
@@ -303,11 +303,11 @@ WALK_CASES = [(2, "bf16", "f32", "bf16"), (8, "f16", "f32", "f16"), (16, "f32", 
 
 @pytest.mark.parametrize("n,t,acc,tout", WALK_CASES, ids=["%d-%s-%s-%s" % c for c in WALK_CASES])
 @pytest.mark.parametrize("grid", [1, 7, 300])
-def test_parity_workgroups_walk_tiles(n, t, acc, tout, grid, monkeypatch):
+def test_parity_workgroups_walk_tiles(n, t, acc, tout, grid, mrr_env):
     count = n * 64 * 2 * (3 * 512 // n + 1) * (16 // OUT_SIZE[tout]) + 13
     announce("rsag tile walk", n, t, acc, tout, count, "grid", grid)
     ins = inputs_for(t, n, count, seed0=70 * n + grid)
-    monkeypatch.setenv("MRR_MAX_GRID", str(grid))
+    mrr_env("MRR_MAX_GRID", str(grid))
     outs = run(ins, t, acc, tout)
     for r in (0, n - 1):
         share = run(ins, t, acc, tout, rank=r, outs=[empty(tout, count, 0x5A) for _ in range(n)])
@@ -320,20 +320,20 @@ def test_parity_workgroups_walk_tiles(n, t, acc, tout, grid, monkeypatch):
             esz = OUT_SIZE[tout]
             assert np.all(raw[:lo * esz] == 0x5A) and np.all(raw[hi * esz:] == 0x5A), \
                 "rank %d share wrote outside its chunk" % r
-    monkeypatch.delenv("MRR_MAX_GRID")
+    mrr_env("MRR_MAX_GRID", None)
     want = oracle.allreduce([bits(x) for x in ins], t, acc, tout)
     check_all(outs, want, tout, "walk n=%d %s/%s/%s grid %d" % (n, t, acc, tout, grid))
 
 
 @pytest.mark.parametrize("n,t,acc,tout", WALK_CASES, ids=["%d-%s-%s-%s" % c for c in WALK_CASES])
-def test_parity_persistent_grid(n, t, acc, tout, monkeypatch):
-    """MRR_LDS_CAP=0 (read per call): no LDS reservation, a persistent grid of
+def test_parity_persistent_grid(n, t, acc, tout, mrr_env):
+    """MRR_LDS_CAP=0 (re-read through mrr_reload_env): no LDS reservation, a persistent grid of
     the table's workgroups per CU striding over the tiles."""
     count = n * 64 * 2 * (3 * 512 // n + 1) * (16 // OUT_SIZE[tout]) + 13
     announce("rsag persistent grid", n, t, acc, tout, count)
     ins = inputs_for(t, n, count, seed0=90 * n + 1)
-    monkeypatch.setenv("MRR_LDS_CAP", "0")
+    mrr_env("MRR_LDS_CAP", "0")
     outs = run(ins, t, acc, tout)
-    monkeypatch.delenv("MRR_LDS_CAP")
+    mrr_env("MRR_LDS_CAP", None)
     want = oracle.allreduce([bits(x) for x in ins], t, acc, tout)
     check_all(outs, want, tout, "persistent n=%d %s/%s/%s" % (n, t, acc, tout))

@@ -12,18 +12,18 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("nbytes", [1, 15, 16, 17, 4096 + 9, 3 * 64 * 4 * 16 + 5, (64 << 20) + 13])
 @pytest.mark.parametrize("mode", ["default", "walk", "persistent"])
-def test_stream_copy_exact(nbytes, mode, monkeypatch):
+def test_stream_copy_exact(nbytes, mode, mrr_env):
     announce("stream copy", nbytes, mode)
     g = torch.Generator().manual_seed(nbytes)
     src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).cuda()
     dst = torch.full((nbytes + 32,), 0xA5, dtype=torch.uint8, device="cuda")
     if mode == "walk":
-        monkeypatch.setenv("MRR_MAX_GRID", "3")
+        mrr_env("MRR_MAX_GRID", "3")
     elif mode == "persistent":
-        monkeypatch.setenv("MRR_LDS_CAP", "0")
+        mrr_env("MRR_LDS_CAP", "0")
     assert mrr.mrr_stream_copy(src, dst, nbytes) == mrr.MRR_OK
     torch.cuda.synchronize()
-    monkeypatch.delenv("MRR_MAX_GRID", raising=False)
-    monkeypatch.delenv("MRR_LDS_CAP", raising=False)
+    mrr_env("MRR_MAX_GRID", None)
+    mrr_env("MRR_LDS_CAP", None)
     assert torch.equal(dst[:nbytes], src)
     assert torch.all(dst[nbytes:] == 0xA5), "wrote past the end"

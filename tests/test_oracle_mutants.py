@@ -59,6 +59,17 @@ MUTANTS = [
      "make_packet(word_at((const uint8_t*)inputs[c], nbytes, w), flag);"),
     ("fp8 encode rounds twice, through f16", "case ORC_FP8: b[0] = narrow_fp8(v); break;",
      "case ORC_FP8: b[0] = narrow_fp8(f16_value(narrow_f16(v))); break;"),
+    ("full-mesh inbox indexed [src][dst]",
+     "uint8_t* slot = inbox + (dst * n + src) * chunk * (size_t)e;",
+     "uint8_t* slot = inbox + (src * n + dst) * chunk * (size_t)e;"),
+    ("full-mesh inbox holds the receiver's own chunk",
+     "const uint8_t* in = (const uint8_t*)inputs[src];",
+     "const uint8_t* in = (const uint8_t*)inputs[dst];"),
+    ("full-mesh semaphore flag in the low word",
+     "sem[(dst * n + src) * 1024 + (size_t)b] = (uint64_t)flag << 32;",
+     "sem[(dst * n + src) * 1024 + (size_t)b] = (uint64_t)flag;"),
+    ("full-mesh last block not signalled", "for (int b = 0; b < nblocks; ++b) sem[",
+     "for (int b = 0; b + 1 < nblocks; ++b) sem["),
 ]
 
 
@@ -86,6 +97,7 @@ def _checks():
         pins.test_pack_unpack_roundtrip,
         lambda o: pins.test_allreduce_packet_expectation(o, "f16", 1001),
         lambda o: pins.test_packet_rsag_expectation(o, "f16", 1001, 4),
+        lambda o: pins.test_fullmesh_expectation(o, "f16", 1001, 4, 3),
         pins.test_fp8fn_decode_vs_torch,
         pins.test_fp8fn_encode_all_f16_brute_force_and_torch,
     ]

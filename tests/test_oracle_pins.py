@@ -551,6 +551,39 @@ def test_packet_rsag_expectation(orc, t, count, nranks):
             assert np.array_equal(ag[d, c, :want.size], want)
 
 
+@pytest.mark.parametrize("t,count,nranks,nblocks", [("f16", 1001, 4, 3), ("fp8", 1023, 8, 1),
+                                                    ("f32", 5, 8, 2), ("bf16", 64, 2, 1024)])
+def test_fullmesh_expectation(orc, t, count, nranks, nblocks):
+    """Full-mesh allreduce: inbox [c][d] holds chunk c of rank d's input
+    (c != d), semaphores [c][d][b < B] hold the flag in their high word, the
+    rest of the image is untouched, and the output is the plain sum.  The
+    expected image is rebuilt here from numpy slicing of the inputs."""
+    import synth
+    if t == "fp8":
+        xs = [_fp8_codes(count, 760 + r) for r in range(nranks)]
+    else:
+        xs = [synth.to_bits_numpy(synth.uniform(t, count, 760 + r)) for r in range(nranks)]
+    e = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[t]
+    chunk, sem_b, box_b = orc.fullmesh_layout(count, t, nranks)
+    assert chunk * e % 16 == 0 and chunk >= -(-count // nranks) and chunk * e - 16 < \
+        -(-count // nranks) * e
+    rng = np.random.default_rng(count)
+    before = rng.integers(0, 256, sem_b + box_b, dtype=np.uint8)  # any prior scratch state
+    img, out = orc.allreduce_fullmesh(xs, t, "f32", 0xABCD0123, nblocks, before)
+    assert np.array_equal(out, orc.allreduce(xs, t, "f32"))
+    want = before.copy()
+    sem = want[:sem_b].view(np.uint64).reshape(nranks, nranks, 1024)
+    box = want[sem_b:].reshape(nranks, nranks, chunk * e)
+    for c in range(nranks):
+        for d in range(nranks):
+            if c == d:
+                continue
+            sem[c, d, :nblocks] = np.uint64(0xABCD0123) << np.uint64(32)
+            part = xs[d].view(np.uint8)[c * chunk * e:(c + 1) * chunk * e]
+            box[c, d, :part.size] = part
+    assert np.array_equal(img, want)
+
+
 # ---------------------------------------------------------------------------
 # OCP FP8 E4M3FN
 # ---------------------------------------------------------------------------
