@@ -31,6 +31,7 @@ DTYPES = {"auto": MRR_AUTO, "f32": MRR_F32, "f16": MRR_F16, "bf16": MRR_BF16,
           "fp8fn": MRR_FP8_E4M3FN, "fp8_e4m3fn": MRR_FP8_E4M3FN}
 MAX_RANKS = 32
 PKT_FLAG_SLOTS = 1024
+MRR_NOALLOC_SCRATCH_BYTES = 32 << 20  # packet scratch of mrr_allreduce_packet_noalloc
 
 
 class MrrError(RuntimeError):
@@ -63,6 +64,7 @@ def load_library() -> ctypes.CDLL:
             "mrr_packet_flag_bytes": ([i], sz),
             "mrr_allreduce_packet": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, vp], i),
             "mrr_allreduce_packet_ex": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, i, i, vp], i),
+            "mrr_allreduce_packet_noalloc": ([pp, pp, sz, i, i, i, u32, vp, vp], i),
             "mrr_packet_reduce": ([pp, vp, sz, i, i, i, u32, u32, u32, vp, vp], i),
             "mrr_allreduce": ([pp, pp, sz, i, i, i, vp, sz, vp, sz, u32, vp, vp], i),
             "mrr_packet_rsag_scratch_bytes": ([sz, i, i], sz),
@@ -267,6 +269,14 @@ def mrr_allreduce_packet_ex(inputs, outputs, scratch, scratch_bytes, flags, coun
         _rank_ptrs(inputs, nranks, nb, "inputs"), _rank_ptrs(outputs, nranks, nb, "outputs"),
         _ptr(scratch), scratch_bytes, _ptr(flags), count, _dt(dtype), _dt(accum), nranks,
         max_spins, _ptr(dev_err), blocks_per_rank, threads, _stream(stream))
+
+
+def mrr_allreduce_packet_noalloc(inputs, outputs, count, dtype, accum, nranks, max_spins,
+                                 dev_err=None, stream=None) -> int:
+    nb = _nbytes(count, dtype)
+    return load_library().mrr_allreduce_packet_noalloc(
+        _rank_ptrs(inputs, nranks, nb, "inputs"), _rank_ptrs(outputs, nranks, nb, "outputs"),
+        count, _dt(dtype), _dt(accum), nranks, max_spins, _ptr(dev_err), _stream(stream))
 
 
 def mrr_packet_rsag_scratch_bytes(count, dtype, nranks) -> int:

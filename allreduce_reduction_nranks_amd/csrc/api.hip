@@ -426,9 +426,62 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
   a.pkts_per_block = (npkt + (uint64_t)B - 1) / (uint64_t)B;
   a.nblocks = (uint32_t)B;
   a.max_spins = max_spins;
+  a.flag_ranks = (uint32_t)nranks;
   return hip_status(launch_packet_allpair(a, nranks, t, tacc, T, batch, (hipStream_t)stream), fn);
 }
 
+mrr_status mrr_allreduce_packet_noalloc(const void* const* inputs, void* const* outputs,
+                                        size_t count, mrr_dtype dtype, mrr_dtype accum,
+                                        int nranks, uint32_t max_spins, uint32_t* dev_err,
+                                        void* stream) {
+  static const char* fn = "mrr_allreduce_packet_noalloc";
+  if (!valid_nranks(nranks)) return refuse(MRR_EUNSUPPORTED, fn, "nranks not in {2,4,8,16,32}");
+  const int t = (int)dtype;
+  const int tacc = accum == MRR_AUTO ? t : (int)accum;
+  if (!inputs || !outputs) return refuse(MRR_EINVAL, fn, "null pointer array");
+  if (!tsize(t) || !packet_supported(nranks, t, tacc))
+    return refuse(MRR_EUNSUPPORTED, fn, "type combination");
+  if (count == 0) return MRR_OK;
+  const size_t need = mrr_packet_scratch_bytes(count, dtype, nranks);
+  if (need == 0 || need > (size_t)MRR_NOALLOC_SCRATCH_BYTES)
+    return refuse(MRR_ESCRATCH, fn,
+                  "nranks^2 * ceil(count * elem_size / 4) * 8 bytes exceed MRR_NOALLOC_SCRATCH_BYTES");
+  const size_t nbytes = count * tsize(t);
+  for (int r = 0; r < nranks; ++r) {
+    if (!inputs[r] || !outputs[r]) return refuse(MRR_EINVAL, fn, "null buffer");
+    if (!aligned(inputs[r], 4) || !aligned(outputs[r], 4))
+      return refuse(MRR_EALIGN, fn, "buffers must be 4-byte aligned");
+  }
+  if (bad_overlap(inputs, nbytes, outputs, nbytes, nranks))
+    return refuse(MRR_EOVERLAP, fn, "output overlaps another buffer");
+  const uint64_t npkt = (nbytes + 3) / 4;
+  const int T = 64;
+  const int batch = packet_allpair_batch(nranks, npkt);
+  int B = 0;
+  mrr_status st = packet_geometry(fn, packet_allpair_kernel(nranks, t, tacc, batch), nranks,
+                                  npkt, T, batch, 0, &B);
+  if (st != MRR_OK) return st;
+  uint8_t* ws = nullptr;
+  const hipError_t e = noalloc_workspace((hipStream_t)stream, &ws);
+  if (e == hipErrorStreamCaptureUnsupported)
+    return refuse(MRR_EINVAL, fn, "the first call on a device must not be under stream capture");
+  if (e != hipSuccess) return hip_status(e, fn);
+  PacketArgs a = {};
+  for (int r = 0; r < nranks; ++r) {
+    a.in[r] = inputs[r];
+    a.out[r] = outputs[r];
+  }
+  a.flags = reinterpret_cast<uint32_t*>(ws);
+  a.scratch = reinterpret_cast<uint64_t*>(ws + kNoAllocFlagBytes);
+  a.dev_err = dev_err;
+  a.nbytes = nbytes;
+  a.npkt = npkt;
+  a.pkts_per_block = (npkt + (uint64_t)B - 1) / (uint64_t)B;
+  a.nblocks = (uint32_t)B;
+  a.max_spins = max_spins;
+  a.flag_ranks = (uint32_t)MRR_MAX_RANKS;
+  return hip_status(launch_packet_allpair(a, nranks, t, tacc, T, batch, (hipStream_t)stream), fn);
+}
 
 // Payload words per full chunk of the two-phase packet allreduce: the RS/AG
 // chunk C = roundup(ceil(count / N), 16 / e) elements, C * e / 4 words.

@@ -80,6 +80,7 @@ struct PacketArgs {
   uint64_t pkts_per_block; // slice width
   uint32_t nblocks;        // B, blocks per rank
   uint32_t max_spins;      // 0 = unbounded
+  uint32_t flag_ranks;     // ranks whose flag slots the call leaves at F (>= N)
 };
 
 // Two-phase (reduce-scatter then all-gather) packet allreduce.
@@ -123,6 +124,14 @@ hipError_t launch_packet_rsag(const PacketRsagArgs& a, int nranks, int t, int ta
 hipError_t launch_pack(const void* src, uint64_t* pkts, size_t nbytes, uint32_t flag,
                        hipStream_t stream);
 hipError_t launch_unpack(const uint64_t* pkts, void* dst, size_t nbytes, hipStream_t stream);
+
+// ---- Library-owned packet workspace (mrr_allreduce_packet_noalloc) ---------
+// Flag slots of every rank count, then packet scratch.
+constexpr size_t kNoAllocFlagBytes = (size_t)kMaxRanks * kFlagSlots * sizeof(uint32_t);
+constexpr size_t kNoAllocPacketBytes = MRR_NOALLOC_SCRATCH_BYTES;
+// Device address of the current device's workspace; the first call on a
+// device clears it on `stream` and must not be under stream capture.
+hipError_t noalloc_workspace(hipStream_t stream, uint8_t** base);
 
 // ---- FP8 codec ----------------------------------------------------------------
 // dir: 0 fp8->f16, 1 fp8->f32, 2 f16->fp8, 3 f32->fp8

@@ -202,10 +202,16 @@ __global__ void __launch_bounds__(kPktMaxThreads) packet_allpair_k(const PacketA
 
   // Flag update: every slot j of rank d with j % B == b, by a thread loop so
   // that a workgroup with fewer threads than slots still covers them all.
+  // A flag area shared by calls of several rank counts (flag_ranks > N) has
+  // the slots of ranks d + N, d + 2N, ... set too, so every slot any later
+  // call reads holds F; no workgroup of this launch reads those.
   __syncthreads();
-  for (uint32_t j = b + threadIdx.x * a.nblocks; j < (uint32_t)kFlagSlots;
-       j += blockDim.x * a.nblocks)
-    my_flags[j] = F;
+  for (uint32_t r = d; r < a.flag_ranks; r += N) {
+    uint32_t* const fl = a.flags + (uint64_t)r * kFlagSlots;
+    for (uint32_t j = b + threadIdx.x * a.nblocks; j < (uint32_t)kFlagSlots;
+         j += blockDim.x * a.nblocks)
+      fl[j] = F;
+  }
 }
 
 // Two-phase packet allreduce, workgroup (rank d, block b), slice b of every

@@ -238,6 +238,43 @@ mrr_status mrr_allreduce_packet_ex(const void* const* inputs, void* const* outpu
                                    int threads, void* stream);
 
 /* --------------------------------------------------------------------------
+ * LL-packet allpair allreduce that allocates nothing, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same operation, results and flag protocol as mrr_allreduce_packet, but the
+ * scratch and the flag slots live in a workspace the library owns: one
+ * statically sized device array per GPU, MRR_NOALLOC_SCRATCH_BYTES of packet
+ * scratch plus the flag slots of 32 ranks (about 32.1 MiB in all), held on
+ * every GPU the library runs on until the process ends.  The call allocates
+ * and frees nothing.
+ *   - A call needs nranks^2 * ceil(count * elem_size / 4) * 8 bytes of packet
+ *     scratch (mrr_packet_scratch_bytes); above MRR_NOALLOC_SCRATCH_BYTES it
+ *     returns MRR_ESCRATCH and launches nothing.  For example 8 ranks take up
+ *     to 256 KiB per rank of f16, 32 ranks up to 16 KiB.
+ *   - The first call on each device clears the workspace with a kernel on
+ *     `stream`, ahead of its own kernel; it must not be made under stream
+ *     capture (MRR_EINVAL, nothing set up).  Later calls may be captured.
+ *   - Every call on one GPU shares that GPU's workspace, which keeps the last
+ *     call's packets and flags; calls of any rank count, size and type
+ *     continue one flag sequence.  Calls that overlap in time on one GPU
+ *     (different streams without ordering, or concurrent graphs) race and may
+ *     hang until max_spins: order them on one stream.
+ *   - The flag sequence wraps after 2^32 - 1 calls; past that a stale packet
+ *     could be taken for a new one (see the flag notes above), so a process
+ *     making that many calls should use mrr_allreduce_packet with its own
+ *     buffers, which it can re-zero.
+ * inputs / outputs / dtype / accum / nranks / max_spins / dev_err as for
+ * mrr_allreduce_packet; geometry is chosen automatically.
+ * ------------------------------------------------------------------------ */
+#define MRR_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+mrr_status mrr_allreduce_packet_noalloc(const void* const* inputs, void* const* outputs,
+                                        size_t count, mrr_dtype dtype, mrr_dtype accum,
+                                        int nranks, uint32_t max_spins, uint32_t* dev_err,
+                                        void* stream);
+
+/* --------------------------------------------------------------------------
  * Two-phase packet allreduce: reduce-scatter then all-gather, both in LL
  * packets (the "packet" allreduce the commit log lists beside allpair, in
  * the entry adding accumDtype; its structure is not on the pages, so this is

@@ -341,3 +341,22 @@ def test_binding_refuses_short_pointer_lists_and_small_tensors(lib):
     # longer lists are fine: the library reads the first nranks entries
     assert mrr.mrr_allreduce_rsag(ins + [fake(9)], outs + [fake(99)], 0, "f16", 4, stream=0) \
         == mrr.MRR_OK
+
+
+def test_noalloc_refusals(lib):
+    """Checks that run before the library touches its workspace or the GPU."""
+    ins = [fake(r) for r in range(8)]
+    outs = [fake(64 + r) for r in range(8)]
+    f = mrr.mrr_allreduce_packet_noalloc
+    assert f(ins, outs, 1024, "f16", "f32", 3, 100, None, 0) == mrr.MRR_EUNSUPPORTED
+    assert f(ins, outs, 1024, "bf16", "f16", 8, 100, None, 0) == mrr.MRR_EUNSUPPORTED
+    assert f(ins, outs, 0, "f16", "f32", 8, 100, None, 0) == mrr.MRR_OK
+    # 8 ranks of f16: at most 32 MiB / (8 * 8 * 8 B) packets of 4 bytes
+    most = mrr.MRR_NOALLOC_SCRATCH_BYTES // (8 * 8 * 8) * 2
+    assert f(ins, outs, most + 1, "f16", "f32", 8, 100, None, 0) == mrr.MRR_ESCRATCH
+    assert f(ins[:2] + [fake(9)], outs[:3], 1 << 30, "f32", "f32", 2, 100, None, 0) \
+        == mrr.MRR_ESCRATCH
+    bad = list(ins)
+    bad[4] += 2
+    assert f(bad, outs, 1024, "f16", "f32", 8, 100, None, 0) == mrr.MRR_EALIGN
+    assert f(ins, [ins[1]] + outs[1:], 1024, "f16", "f32", 8, 100, None, 0) == mrr.MRR_EOVERLAP
