@@ -69,6 +69,8 @@ def load_library() -> ctypes.CDLL:
             "mrr_allreduce": ([pp, pp, sz, i, i, i, vp, sz, vp, sz, u32, vp, vp], i),
             "mrr_packet_rsag_scratch_bytes": ([sz, i, i], sz),
             "mrr_allreduce_packet_rsag": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, i, i, vp], i),
+            "mrr_fullmesh_scratch_bytes": ([sz, i, i], sz),
+            "mrr_allreduce_fullmesh": ([pp, pp, vp, sz, vp, sz, i, i, i, u32, vp, i, i, vp], i),
             "mrr_pack": ([vp, vp, sz, u32, vp], i),
             "mrr_unpack": ([vp, vp, sz, vp], i),
             "mrr_fp8b15_to_f16": ([vp, vp, sz, vp], i),
@@ -290,6 +292,22 @@ def mrr_allreduce_packet_rsag(inputs, outputs, scratch, scratch_bytes, flags, co
     _room(scratch, scratch_bytes, "scratch")
     _room(flags, 4 * PKT_FLAG_SLOTS * max(0, nranks), "flags")
     return load_library().mrr_allreduce_packet_rsag(
+        _rank_ptrs(inputs, nranks, nb, "inputs"), _rank_ptrs(outputs, nranks, nb, "outputs"),
+        _ptr(scratch), scratch_bytes, _ptr(flags), count, _dt(dtype), _dt(accum), nranks,
+        max_spins, _ptr(dev_err), blocks_per_rank, threads, _stream(stream))
+
+
+def mrr_fullmesh_scratch_bytes(count, dtype, nranks) -> int:
+    return load_library().mrr_fullmesh_scratch_bytes(count, _dt(dtype), nranks)
+
+
+def mrr_allreduce_fullmesh(inputs, outputs, scratch, scratch_bytes, flags, count, dtype, accum,
+                           nranks, max_spins, dev_err=None, blocks_per_rank=0, threads=0,
+                           stream=None) -> int:
+    nb = _nbytes(count, dtype)
+    _room(scratch, scratch_bytes, "scratch")
+    _room(flags, 4 * PKT_FLAG_SLOTS * max(0, nranks), "flags")
+    return load_library().mrr_allreduce_fullmesh(
         _rank_ptrs(inputs, nranks, nb, "inputs"), _rank_ptrs(outputs, nranks, nb, "outputs"),
         _ptr(scratch), scratch_bytes, _ptr(flags), count, _dt(dtype), _dt(accum), nranks,
         max_spins, _ptr(dev_err), blocks_per_rank, threads, _stream(stream))

@@ -533,6 +533,70 @@ mrr_status mrr_allreduce_packet_rsag(const void* const* inputs, void* const* out
   return hip_status(launch_packet_rsag(a, nranks, t, tacc, T, (hipStream_t)stream), fn);
 }
 
+// Chunk width of the two-phase packet and full-mesh allreduces, in elements:
+// C = roundup(ceil(count / N), 16 / e).
+static uint64_t chunk16_elems(size_t count, int e, int nranks) {
+  const uint64_t per = (count + (uint64_t)nranks - 1) / (uint64_t)nranks;
+  const uint64_t vw = 16 / (uint64_t)e;
+  return (per + vw - 1) / vw * vw;
+}
+
+// Full-mesh scratch: N * N * MRR_PKT_FLAG_SLOTS semaphores of 8 bytes, then
+// N * N inboxes of one chunk each.
+static size_t fullmesh_sem_bytes(int nranks) {
+  return (size_t)nranks * (size_t)nranks * MRR_PKT_FLAG_SLOTS * 8;
+}
+
+size_t mrr_fullmesh_scratch_bytes(size_t count, mrr_dtype dtype, int nranks) {
+  const int e = tsize((int)dtype);
+  if (!e || nranks <= 0 || nranks > MRR_MAX_RANKS || !packet_count_ok(count, e)) return 0;
+  return fullmesh_sem_bytes(nranks) +
+         (size_t)nranks * (size_t)nranks * chunk16_elems(count, e, nranks) * (size_t)e;
+}
+
+mrr_status mrr_allreduce_fullmesh(const void* const* inputs, void* const* outputs, void* scratch,
+                                  size_t scratch_bytes, uint32_t* flags, size_t count,
+                                  mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                  uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
+                                  int threads, void* stream) {
+  static const char* fn = "mrr_allreduce_fullmesh";
+  const int t = (int)dtype;
+  const int tacc = accum == MRR_AUTO ? t : (int)accum;
+  if (threads != 0 && (threads < 64 || threads > fullmesh_max_threads() || threads % 64 != 0))
+    return refuse(MRR_EINVAL, fn, "threads must be a multiple of 64 in [64, 512]");
+  mrr_status st = packet_checks(fn, inputs, outputs, scratch, scratch_bytes,
+                                mrr_fullmesh_scratch_bytes(count, dtype, nranks), flags, count, t,
+                                tacc, nranks, blocks_per_rank, 0);
+  if (st != MRR_OK || count == 0) return st;
+  if (!aligned(scratch, 16)) return refuse(MRR_EALIGN, fn, "scratch must be 16-byte aligned");
+  for (int r = 0; r < nranks; ++r)
+    if (!aligned(inputs[r], 16) || !aligned(outputs[r], 16))
+      return refuse(MRR_EALIGN, fn, "inputs and outputs must be 16-byte aligned");
+  const int e = tsize(t);
+  const uint64_t chunk = chunk16_elems(count, e, nranks);
+  const uint64_t cvec = chunk * (uint64_t)e / 16;
+  const int T = threads ? threads : 64;
+  int B = 0;
+  st = packet_geometry(fn, fullmesh_kernel(nranks, t, tacc), nranks, cvec, T, 1, blocks_per_rank,
+                       &B);
+  if (st != MRR_OK) return st;
+  FullmeshArgs a = {};
+  for (int r = 0; r < nranks; ++r) {
+    a.in[r] = inputs[r];
+    a.out[r] = outputs[r];
+  }
+  a.sem = (uint64_t*)scratch;
+  a.inbox = (uint8_t*)scratch + fullmesh_sem_bytes(nranks);
+  a.flags = flags;
+  a.dev_err = dev_err;
+  a.count = count;
+  a.chunk = chunk;
+  a.vec_per_block = (cvec + (uint64_t)B - 1) / (uint64_t)B;
+  a.nblocks = (uint32_t)B;
+  a.max_spins = max_spins;
+  return hip_status(launch_fullmesh(a, nranks, t, tacc, T, (hipStream_t)stream), fn);
+}
+
 mrr_status mrr_allreduce_packet(const void* const* inputs, void* const* outputs, void* scratch,
                                 size_t scratch_bytes, uint32_t* flags, size_t count,
                                 mrr_dtype dtype, mrr_dtype accum, int nranks,

@@ -98,6 +98,21 @@ struct PacketRsagArgs {
   uint32_t max_spins;
 };
 
+// Full-mesh allreduce: plain-data inboxes signalled by semaphores.
+struct FullmeshArgs {
+  const void* in[kMaxRanks];
+  void* out[kMaxRanks];
+  uint64_t* sem;            // [dst][src][kFlagSlots], flag in the high half
+  uint8_t* inbox;           // [dst][src][chunk * elem_size]
+  uint32_t* flags;          // [rank][kFlagSlots]
+  uint32_t* dev_err;        // may be null
+  uint64_t count;           // elements per rank
+  uint64_t chunk;           // C, elements per chunk (a multiple of 16 / elem_size)
+  uint64_t vec_per_block;   // 16-byte vectors of each chunk per block
+  uint32_t nblocks;         // B, blocks per rank
+  uint32_t max_spins;       // 0 = unbounded
+};
+
 struct PacketReduceArgs {
   const uint64_t* in[kMaxRanks];
   uint64_t* out;
@@ -121,6 +136,11 @@ hipError_t launch_packet_reduce(const PacketReduceArgs& a, int nranks, int t, in
 const void* packet_rsag_kernel(int nranks, int t, int tacc);
 hipError_t launch_packet_rsag(const PacketRsagArgs& a, int nranks, int t, int tacc, int threads,
                               hipStream_t stream);
+// Full-mesh allreduce (same (type, accumulator) pairs as the packet kernels).
+int fullmesh_max_threads();
+const void* fullmesh_kernel(int nranks, int t, int tacc);
+hipError_t launch_fullmesh(const FullmeshArgs& a, int nranks, int t, int tacc, int threads,
+                           hipStream_t stream);
 hipError_t launch_pack(const void* src, uint64_t* pkts, size_t nbytes, uint32_t flag,
                        hipStream_t stream);
 hipError_t launch_unpack(const uint64_t* pkts, void* dst, size_t nbytes, hipStream_t stream);

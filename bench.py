@@ -477,12 +477,14 @@ def bench_packet(args, torch, mrr, synth):
     ins = [x.to("cuda") for x in synth.rank_inputs("uniform", t, n, count, args.seed0)]
     outs = [torch.empty(count, dtype=torch.float16, device="cuda") for _ in range(n)]
     two_phase = args.algo == "rsag"
-    sbytes = (mrr.mrr_packet_rsag_scratch_bytes if two_phase else mrr.mrr_packet_scratch_bytes)(
-        count, t, n)
-    scratch = torch.zeros(sbytes // 8, dtype=torch.int64, device="cuda")
+    fullmesh = args.algo == "fullmesh"
+    sbytes = {"allpair": mrr.mrr_packet_scratch_bytes, "rsag": mrr.mrr_packet_rsag_scratch_bytes,
+              "fullmesh": mrr.mrr_fullmesh_scratch_bytes}[args.algo](count, t, n)
+    scratch = torch.zeros(-(-sbytes // 8), dtype=torch.int64, device="cuda")
     flags = torch.zeros(n * mrr.PKT_FLAG_SLOTS, dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    entry = mrr.mrr_allreduce_packet_rsag if two_phase else mrr.mrr_allreduce_packet_ex
+    entry = {"allpair": mrr.mrr_allreduce_packet_ex, "rsag": mrr.mrr_allreduce_packet_rsag,
+             "fullmesh": mrr.mrr_allreduce_fullmesh}[args.algo]
 
     def step():
         st = entry(ins, outs, scratch, sbytes, flags, count, t, "f32", n, 4_000_000, err,
@@ -491,7 +493,7 @@ def bench_packet(args, torch, mrr, synth):
             raise mrr.MrrError(st)
 
     S = count * 2
-    graph = use_graph(args, 3 * n * S + 4 * n * (n - 1) * S)
+    graph = use_graph(args, n * S)
     eager_us = None
     prime = lambda: poison(outs)  # noqa: E731
     if graph:
@@ -504,8 +506,13 @@ def bench_packet(args, torch, mrr, synth):
     # allpair: send reads NS, packets 2N(N-1)S written and read, own input NS, outputs NS.
     # two-phase: input NS; rs packets 2(N-1)S written and read; own chunk S; outputs NS;
     # ag packets 2(N-1)S written and read.
-    alg_bytes = (3 * n * S + 8 * (n - 1) * S) if two_phase else (3 * n * S + 4 * n * (n - 1) * S)
-    name = "two-phase (RS + AG) packet" if two_phase else "LL-packet allpair"
+    # full-mesh: peers' chunks (N-1)S read, written to inboxes and read back; own
+    # chunks S; outputs NS.
+    alg_bytes = {"allpair": 3 * n * S + 4 * n * (n - 1) * S,
+                 "rsag": 3 * n * S + 8 * (n - 1) * S,
+                 "fullmesh": (4 * n - 2) * S}[args.algo]
+    name = {"allpair": "LL-packet allpair", "rsag": "two-phase (RS + AG) packet",
+            "fullmesh": "full-mesh (plain data + semaphores)"}[args.algo]
     result = {
         "metric": "%s allreduce latency" % name, "value": round(kern_ms * 1e3, 3),
         "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -693,8 +700,9 @@ def main():
     ap.add_argument("--fp8", default="e4m3b15", choices=["e4m3b15", "e4m3fn"],
                     help="c4: FP8 input format")
     ap.add_argument("--size", type=int, default=1024, help="c3 / custom: KiB per rank")
-    ap.add_argument("--algo", default="allpair", choices=["allpair", "rsag"],
-                    help="c3: allpair packets or the two-phase (RS + AG) packet variant")
+    ap.add_argument("--algo", default="allpair", choices=["allpair", "rsag", "fullmesh"],
+                    help="c3: allpair packets, the two-phase (RS + AG) packet variant, or the "
+                         "full-mesh allreduce (plain data + semaphores)")
     ap.add_argument("--blocks", type=int, default=0, help="c3: blocks per rank (0 = auto)")
     ap.add_argument("--threads", type=int, default=0, help="c3: threads (0 = auto)")
     ap.add_argument("--seed0", type=int, default=0)

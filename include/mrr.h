@@ -305,6 +305,45 @@ mrr_status mrr_allreduce_packet_rsag(const void* const* inputs, void* const* out
                                      int threads, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Full-mesh allreduce (commit history: the entries adding accumDtype and
+ * ROCm FP8 E4M3B15 support name a "fullmesh" allreduce beside the allpair
+ * packet one; its steps are not on the pages, so this is the plain reading of
+ * the name: every rank talks to every peer directly, by writes only, in plain
+ * data rather than LL packets, each delivery signalled by a flag written
+ * after it).  Chunks as the two-phase packet allreduce: C = roundup(ceil(count
+ * / N), 16 / elem_size) elements, chunk c = elements [c*C, min((c+1)*C,
+ * count)).  Workgroup (rank d, block b) takes slice b of every chunk:
+ *   1. it writes slice b of chunk c of inputs[d] into inbox [c][d] of the
+ *      scratch, for every peer c != d;
+ *   2. it sets semaphore [c][d][b] = (uint64)F << 32 for every peer c != d
+ *      (agent-scope release after the data);
+ *   3. it waits until semaphore [d][s][b] carries F for every peer s
+ *      (agent-scope acquire; bounded by max_spins), sums slice b of chunk d
+ *      in rank order 0..nranks-1 -- its own part from inputs[d], the others
+ *      from inbox [d][s] -- and writes it to chunk d of every outputs[k];
+ *   4. it sets the flag slots j of rank d with j % B == b to F.
+ * Per call it moves about (4N - 2) * S bytes (S = count * elem_size), against
+ * 2N * S for RS/AG.
+ * scratch: device, 16-byte aligned, mrr_fullmesh_scratch_bytes() bytes: the
+ *   semaphores, N * N * MRR_PKT_FLAG_SLOTS uint64 [dst][src][slot], then the
+ *   inboxes, N * N * C * elem_size bytes [dst][src][chunk].  Zero it once
+ *   before first use (a semaphore must never hold a flag the sequence has
+ *   not reached).  It may be shared with the packet entry points and the same
+ *   flag buffer.
+ * inputs / outputs: 16-byte aligned (MRR_EALIGN); outputs[k] may be
+ *   inputs[k] exactly.  flags, dtype, accum, max_spins, dev_err,
+ *   blocks_per_rank, threads and errors as mrr_allreduce_packet_ex (the
+ *   auto geometry covers one 16-byte vector per lane per chunk).
+ * ------------------------------------------------------------------------ */
+size_t mrr_fullmesh_scratch_bytes(size_t count, mrr_dtype dtype, int nranks);
+
+mrr_status mrr_allreduce_fullmesh(const void* const* inputs, void* const* outputs, void* scratch,
+                                  size_t scratch_bytes, uint32_t* flags, size_t count,
+                                  mrr_dtype dtype, mrr_dtype accum, int nranks,
+                                  uint32_t max_spins, uint32_t* dev_err, int blocks_per_rank,
+                                  int threads, void* stream);
+
+/* --------------------------------------------------------------------------
  * One-call allreduce with algorithm selection ("Support 2 ranks in
  * AllreduceRsAgZeroCopy", section "why": selectors pick RS/AG zero-copy above
  * a message size and packets below it; section "what changed": rank counts

@@ -360,3 +360,37 @@ def test_noalloc_refusals(lib):
     bad[4] += 2
     assert f(bad, outs, 1024, "f16", "f32", 8, 100, None, 0) == mrr.MRR_EALIGN
     assert f(ins, [ins[1]] + outs[1:], 1024, "f16", "f32", 8, 100, None, 0) == mrr.MRR_EOVERLAP
+
+
+def test_fullmesh_sizes_and_refusals(lib):
+    # semaphores N*N*1024*8, then N*N inboxes of C = roundup(ceil(count/N), 16/e) elements
+    assert mrr.mrr_fullmesh_scratch_bytes(1000, "f16", 8) == 8 * 8 * 1024 * 8 + 8 * 8 * 128 * 2
+    assert mrr.mrr_fullmesh_scratch_bytes(5, "f32", 8) == 8 * 8 * 1024 * 8 + 8 * 8 * 4 * 4
+    assert mrr.mrr_fullmesh_scratch_bytes(1, "fp8", 33) == 0
+    assert mrr.mrr_fullmesh_scratch_bytes(1, "auto", 2) == 0
+
+    def fm(n=8, count=4096, t="f16", acc="f32", ins=None, outs=None, scratch=None, sbytes=None,
+           flags=None, blocks=0, threads=0):
+        ins = ins if ins is not None else [fake(r) for r in range(n)]
+        outs = outs if outs is not None else [fake(64 + r) for r in range(n)]
+        scratch = scratch if scratch is not None else fake(200)
+        sbytes = sbytes if sbytes is not None else mrr.mrr_fullmesh_scratch_bytes(count, t, n)
+        flags = flags if flags is not None else fake(300)
+        return mrr.mrr_allreduce_fullmesh(ins, outs, scratch, sbytes, flags, count, t, acc, n,
+                                          1000, 0, blocks, threads, stream=0)
+
+    assert fm(n=6) == mrr.MRR_EUNSUPPORTED
+    assert fm(t="bf16", acc="f16") == mrr.MRR_EUNSUPPORTED
+    assert fm(sbytes=mrr.mrr_fullmesh_scratch_bytes(4096, "f16", 8) - 16) == mrr.MRR_ESCRATCH
+    assert fm(threads=96) == mrr.MRR_EINVAL
+    assert fm(threads=1024) == mrr.MRR_EINVAL
+    assert fm(blocks=1025) == mrr.MRR_EINVAL
+    ins = [fake(r) for r in range(8)]
+    ins[3] += 4  # element-aligned, not 16-byte aligned: the full-mesh path needs 16
+    assert fm(ins=ins) == mrr.MRR_EALIGN
+    assert fm(scratch=fake(200, off=8)) == mrr.MRR_EALIGN
+    assert fm(flags=fake(200, off=64)) == mrr.MRR_EOVERLAP
+    outs = [fake(64 + r) for r in range(8)]
+    outs[2] = ins[5]
+    assert fm(outs=outs) == mrr.MRR_EOVERLAP
+    assert fm(count=0) == mrr.MRR_OK
