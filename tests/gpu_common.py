@@ -1,11 +1,14 @@
 """Helpers shared by the GPU parity tests: device buffers, bit-level
 comparison against the oracle, and progress prints that name each case
 before it touches the GPU."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
 
+import oracle
 import synth
 
 TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8,
@@ -61,3 +64,52 @@ def inputs_for(t: str, n: int, count: int, seed0: int, kind=None, device="cuda")
     return [x.to(device) for x in synth.rank_inputs(kind, t, n, count, seed0, device="cpu")] \
         if device == "cuda" and count * n <= (1 << 24) else \
         synth.rank_inputs(kind, t, n, count, seed0, device=device)
+
+
+NP_BITS = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8,
+           "fp8fn": np.uint8}
+
+
+def host_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may use, at most
+    OMP_NUM_THREADS when set, and at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(16, n))
+
+
+def oracle_allreduce_threaded(host_ins, t, acc, tout, block=1 << 22):
+    """oracle.allreduce over disjoint element blocks on host threads (its
+    ctypes calls release the GIL).  Each element is still summed by one
+    oracle call in rank order, so the result is the oracle's, whole."""
+    count = host_ins[0].size
+    want = np.empty(count, dtype=NP_BITS[tout])
+    orc = oracle.default()
+
+    def run(lo):
+        hi = min(count, lo + block)
+        orc.allreduce([x[lo:hi] for x in host_ins], t, acc, tout, out=want[lo:hi])
+
+    with ThreadPoolExecutor(host_threads()) as ex:
+        for f in [ex.submit(run, lo) for lo in range(0, count, block)]:
+            f.result()
+    return want
+
+
+def assert_outputs_match(outs, want, t, what):
+    """Every element of every output equals the oracle's bits (NaN against NaN
+    counts as equal): compared on the GPU, with a host comparison for the
+    message when something differs."""
+    ints = {1: (np.uint8, torch.uint8), 2: (np.int16, torch.int16),
+            4: (np.int32, torch.int32)}[SIZE[t]]
+    w = torch.from_numpy(np.ascontiguousarray(want).view(ints[0])).to("cuda")
+    for k, o in enumerate(outs):
+        got = o.view(-1).view(torch.uint8).view(ints[1])
+        assert got.numel() == w.numel(), (what, got.numel(), w.numel())
+        if not torch.equal(got, w):
+            assert_bits_equal(bits(o), want, t, "%s out[%d]" % (what, k))

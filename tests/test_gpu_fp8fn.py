@@ -9,7 +9,8 @@ import torch
 
 import allreduce_reduction_nranks_amd as mrr
 import oracle
-from gpu_common import announce, assert_bits_equal, bits, empty, inputs_for
+from gpu_common import (announce, assert_bits_equal, assert_outputs_match, bits, empty, inputs_for,
+                        oracle_allreduce_threaded)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,9 +84,10 @@ def test_rsag_fn_unaligned_buffers():
 
 
 @pytest.mark.parametrize("tout", [T, "f32"])
-def test_rsag_fn_full_size_sampled(tout):
-    """8 ranks x 64 MiB of E4M3FN, f32 accumulation, pooled layout, sampled;
-    E4M3FN outputs, and f32 outputs (the 128-lane-tile kernel)."""
+def test_rsag_fn_full_size_whole(tout):
+    """8 ranks x 64 MiB of E4M3FN, f32 accumulation, pooled layout; E4M3FN
+    outputs, and f32 outputs (the 128-lane-tile kernel).  A sampled pre-check,
+    then every element of every output against the oracle (host threads)."""
     n, count = 8, 64 << 20
     announce("fn rsag 8 x 64 MiB ->", tout)
     pool_in, ins = mrr.alloc_rank_buffers(n, count, T)
@@ -98,7 +100,9 @@ def test_rsag_fn_full_size_sampled(tout):
         np.random.default_rng(8).integers(0, count, 1 << 17), [0, count - 1]]))).cuda()
     want = oracle.allreduce([bits(x[idx]) for x in ins], T, "f32", tout)
     for k in range(n):
-        assert_bits_equal(bits(outs[k][idx]), want, tout, "out[%d]" % k)
+        assert_bits_equal(bits(outs[k][idx]), want, tout, "out[%d] sampled" % k)
+    want = oracle_allreduce_threaded([bits(x) for x in ins], T, "f32", tout)
+    assert_outputs_match(outs, want, tout, "8 x 64 MiB -> %s whole" % tout)
 
 
 @pytest.mark.parametrize("n", [3, 5, 12, 31])

@@ -9,7 +9,8 @@ import torch
 
 import allreduce_reduction_nranks_amd as mrr
 import oracle
-from gpu_common import TORCH, announce, assert_bits_equal, bits, empty, inputs_for
+from gpu_common import (TORCH, announce, assert_bits_equal, assert_outputs_match, bits, empty,
+                        inputs_for, oracle_allreduce_threaded)
 
 pytestmark = pytest.mark.gpu
 
@@ -273,9 +274,10 @@ def test_full_size_fp8_eight_ranks_32mib(tout):
 
 
 @pytest.mark.parametrize("n", RANKS)
-def test_rank_sweep_256mib_bf16_sampled(n):
-    """N x 256 MiB of bf16 ~N(0,1) (inputs drawn on the device): sampled
-    outputs against the oracle, chunk edges included, all outputs identical."""
+def test_rank_sweep_256mib_bf16_whole(n):
+    """N x 256 MiB of bf16 ~N(0,1) (inputs drawn on the device): a sampled
+    pre-check (chunk edges included), then every element of every output
+    against the oracle, run over the whole inputs on host threads."""
     count, t = 256 * (1 << 20) // 2, "bf16"
     announce("rsag sweep 256MiB bf16 n=%d" % n)
     ins = inputs_for(t, n, count, seed0=1000, device="cuda")
@@ -283,13 +285,15 @@ def test_rank_sweep_256mib_bf16_sampled(n):
     assert mrr.mrr_allreduce_rsag(ins, outs, count, t, n) == mrr.MRR_OK
     torch.cuda.synchronize()
     idx = sample_indices(count, n, CHUNK_ALIGN[t], np.random.default_rng(n))
-    sub_in = [bits(x[idx]) for x in ins]
-    want = oracle.allreduce(sub_in, t, "f32")
+    want = oracle.allreduce([bits(x[idx]) for x in ins], t, "f32")
     for k in range(n):
-        assert_bits_equal(bits(outs[k][idx]), want, t, "n=%d out[%d]" % (n, k))
-        if k:
-            assert torch.equal(outs[k].view(torch.int16), outs[0].view(torch.int16))
-    del ins, outs
+        assert_bits_equal(bits(outs[k][idx]), want, t, "n=%d out[%d] sampled" % (n, k))
+    host = [bits(x) for x in ins]
+    del ins
+    want = oracle_allreduce_threaded(host, t, "f32", t)
+    del host
+    assert_outputs_match(outs, want, t, "n=%d whole" % n)
+    del outs
     torch.cuda.empty_cache()
 
 
