@@ -48,6 +48,9 @@ _lib = None
 def load_library() -> ctypes.CDLL:
     """Loads libmrr.so (once).  Raises if it has not been built."""
     global _lib
+    lib = _lib
+    if lib is not None:  # loaded: no lock on the per-call path
+        return lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -106,10 +109,13 @@ def _ptrs(xs):
 
 
 def _dt(d) -> int:
+    v = DTYPES.get(d) if type(d) is str else None
+    if v is not None:
+        return v
     if isinstance(d, int):
         return d
     if isinstance(d, str):
-        return DTYPES[d]
+        raise KeyError("unknown type name %r" % d)
     import torch
     return {torch.float32: MRR_F32, torch.float16: MRR_F16, torch.bfloat16: MRR_BF16,
             torch.uint8: MRR_FP8_E4M3B15}[d]
@@ -121,7 +127,7 @@ _ESIZE = {MRR_F32: 4, MRR_F16: 2, MRR_BF16: 2, MRR_FP8_E4M3B15: 1, MRR_FP8_E4M3F
 def _nbytes(count, dtype) -> int:
     """Bytes of `count` elements of dtype (0 for AUTO or an unknown id, which
     the C ABI refuses on its own)."""
-    return max(0, int(count)) * _ESIZE.get(_dt(dtype), 0)
+    return (count if count > 0 else 0) * _ESIZE.get(_dt(dtype), 0)
 
 
 def _room(x, nbytes: int, what: str) -> None:
@@ -143,15 +149,16 @@ def _rank_ptrs(xs, nranks: int, nbytes: int, what: str):
         raise ValueError("%s has %d entries, nranks is %d" % (what, len(xs), nranks))
     ptrs = []
     for x in xs:
-        if x is None:
-            ptrs.append(0)
-        elif isinstance(x, int):
-            ptrs.append(x)
+        if x is None or type(x) is int:
+            ptrs.append(x or 0)
         else:
             if x.nbytes < nbytes and len(ptrs) < nranks:
                 _room(x, nbytes, "%s[%d]" % (what, len(ptrs)))
             ptrs.append(x.data_ptr())
-    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return (_VP * len(ptrs))(*ptrs)
+
+
+_VP = ctypes.c_void_p
 
 
 _raw_stream = None
@@ -165,10 +172,11 @@ def _stream(stream) -> int:
     a third of an eager call's host cost)."""
     global _raw_stream
     if stream is None:
-        import torch
         if _raw_stream is None:
+            import torch
             getter = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-            _raw_stream = (lambda: int(getter(torch.cuda.current_device()))) if getter else \
+            device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+            _raw_stream = (lambda: getter(device())) if getter else \
                 (lambda: int(torch.cuda.current_stream().cuda_stream))
         return _raw_stream()
     if isinstance(stream, int):

@@ -27,6 +27,7 @@ struct EnvOverrides {
   std::atomic<int> rsag_small{1};   // MRR_RSAG_SMALL=0 turns the small-call route off
   std::atomic<int> codec_u{0};      // MRR_CODEC_U=<u>, 0 = the launch table
   std::atomic<int> codec_wpc{0};    // MRR_CODEC_WPC=<w>, 0 = the launch table
+  std::atomic<int> cooperative{0};  // MRR_COOPERATIVE=1: cross-workgroup kernels launch cooperatively
 };
 EnvOverrides g_env;
 
@@ -49,6 +50,7 @@ void read_env() {
   g_env.rsag_small.store(!(sm && sm[0] == '0'), std::memory_order_relaxed);
   g_env.codec_u.store(env_atoi("MRR_CODEC_U"), std::memory_order_relaxed);
   g_env.codec_wpc.store(env_atoi("MRR_CODEC_WPC"), std::memory_order_relaxed);
+  g_env.cooperative.store(env_atoi("MRR_COOPERATIVE") == 1, std::memory_order_relaxed);
 }
 
 struct EnvAtLoad {
@@ -179,6 +181,28 @@ int rsag_any_m_override() { return g_env.rsag_any_m.load(std::memory_order_relax
 bool rsag_small_enabled() { return g_env.rsag_small.load(std::memory_order_relaxed) != 0; }
 int codec_u_override() { return g_env.codec_u.load(std::memory_order_relaxed); }
 int codec_wpc_override() { return g_env.codec_wpc.load(std::memory_order_relaxed); }
+
+// MRR_COOPERATIVE=1: the kernels whose workgroups wait for each other (the
+// packet allreduces and the full mesh) launch through
+// hipLaunchCooperativeKernel, so a grid that cannot be resident at once is a
+// launch error (MRR_EHIP) instead of a wait.  Measured on MI355X, 8 ranks of
+// f16: about 15 us more per eager call (16 KiB allpair 10.3 -> 24.4 us,
+// full mesh 9.2 -> 25.4 us), and 4-14 us more per graph replay, so it is
+// off by default; captured calls launch cooperatively too.
+bool cooperative_launch_enabled() { return g_env.cooperative.load(std::memory_order_relaxed) != 0; }
+
+hipError_t launch_resident(const void* kernel, dim3 grid, dim3 block, void* args,
+                           hipStream_t stream) {
+  void* params[] = {args};
+  hipError_t e = cooperative_launch_enabled()
+                     ? hipLaunchCooperativeKernel(kernel, grid, block, params, 0, stream)
+                     : hipLaunchKernel(kernel, grid, block, params, 0, stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // the error is returned here; do not leave it to the next call
+    return e;
+  }
+  return hipGetLastError();
+}
 
 // Workgroups of `kernel` at `threads` threads that fit on the device at once,
 // cached per (kernel, threads, device): the occupancy query costs
@@ -575,10 +599,26 @@ mrr_status mrr_allreduce_fullmesh(const void* const* inputs, void* const* output
   const int e = tsize(t);
   const uint64_t chunk = chunk16_elems(count, e, nranks);
   const uint64_t cvec = chunk * (uint64_t)e / 16;
-  const int T = threads ? threads : 64;
-  int B = 0;
-  st = packet_geometry(fn, fullmesh_kernel(nranks, t, tacc), nranks, cvec, T, 1, blocks_per_rank,
-                       &B);
+  // Auto geometry: 256-lane workgroups, one vector per lane per chunk, at
+  // most kFmAutoWorkgroups workgroups in all.  Every workgroup pays one
+  // agent-scope release (an L2 writeback) and one acquire (an L2
+  // invalidate), so fewer, wider workgroups win once there is enough work:
+  // measured on MI355X, 8 ranks of f16, 64-lane workgroups with one vector
+  // per lane took 16.2 / 53.6 / 267 us at 256 KiB / 1 MiB / 4 MiB per rank,
+  // 256 lanes 7.3 / 14.6 / 60.6 us, and 256 lanes with 16 blocks per rank
+  // 8.0 / 12.9 / 30.2 us (16 MiB: 129 us; 64 blocks 116 us).
+  constexpr int kFmAutoThreads = 256;
+  constexpr int kFmAutoWorkgroups = 256;
+  const int T = threads ? threads : kFmAutoThreads;
+  int B = blocks_per_rank;
+  if (B == 0) {
+    const uint64_t want = (cvec + (uint64_t)T - 1) / (uint64_t)T;
+    const uint64_t cap = kFmAutoWorkgroups / nranks > 1 ? kFmAutoWorkgroups / nranks : 1;
+    B = (int)(want < 1 ? 1 : want > cap ? cap : want);
+    const int fit = max_resident_blocks(fullmesh_kernel(nranks, t, tacc), T) / nranks;
+    if (B > fit && fit >= 1) B = fit;
+  }
+  st = packet_geometry(fn, fullmesh_kernel(nranks, t, tacc), nranks, cvec, T, 1, B, &B);
   if (st != MRR_OK) return st;
   FullmeshArgs a = {};
   for (int r = 0; r < nranks; ++r) {

@@ -84,32 +84,63 @@ __global__ void __launch_bounds__(kFmMaxThreads) fullmesh_k(const FullmeshArgs a
   const uint64_t v_hi = v_lo + a.vec_per_block < cvec ? v_lo + a.vec_per_block : cvec;
   const uint64_t slot_bytes = chunk * Ty<T>::size;
 
-  // 1. push slice b of chunk c of rank d's input into inbox [c][d]
-#pragma unroll
-  for (int c = 0; c < N; ++c) {
-    if ((uint32_t)c == d) continue;
-    const uint64_t nc = chunk_elems(a.count, chunk, (uint32_t)c);
-    uint8_t* const slot = a.inbox + ((uint64_t)c * N + d) * slot_bytes;
+  // The buffer's one partial vector (count % V elements, if any) lies at
+  // vector pv of chunk pc; it is moved element by element, apart from the
+  // whole vectors, by the lane of the workgroup whose slice holds it.
+  const uint64_t tail_first = a.count / V * V;
+  const bool has_tail = tail_first < a.count;
+  const uint32_t pc = (uint32_t)(tail_first / chunk);
+  const uint64_t pv = (tail_first - (uint64_t)pc * chunk) / V;
+  const bool tail_lane = has_tail && pv >= v_lo && pv < v_hi &&
+                         (pv - v_lo) % blockDim.x == threadIdx.x;
+
+  // 1. push slice b of chunk c of rank d's input into inbox [c][d], peers
+  // in groups of up to 8: a lane loads its vector of every chunk of a group
+  // before it stores any, one memory round trip per group instead of one per
+  // peer (the compiler cannot hoist a load above a store that may alias it).
+  // Every lane issues all loads of a group unconditionally (a lane with
+  // nothing to send for chunk c reads vector 0 of the input instead, which
+  // exists whenever a whole vector does), so no load waits on a branch.
+  constexpr int GP = N < 8 ? N : 8;
+  if (a.count >= (uint64_t)V) {
     for (uint64_t v = v_lo + threadIdx.x; v < v_hi; v += blockDim.x) {
       const uint64_t first = v * V;
-      if (first >= nc) break;
-      if (first + V <= nc) {
-        reinterpret_cast<u32x4*>(slot)[v] =
-            reinterpret_cast<const u32x4*>(a.in[d])[(uint64_t)c * cvec + v];
-      } else {
-        copy_elems<T>(a.in[d], (uint64_t)c * chunk + first, slot, first, nc - first);
+#pragma unroll 1
+      for (int c0 = 0; c0 < N; c0 += GP) {
+        u32x4 buf[GP];
+        bool send[GP];
+#pragma unroll
+        for (int j = 0; j < GP; ++j) {
+          const uint32_t c = (uint32_t)(c0 + j);
+          send[j] = c != d && first + V <= chunk_elems(a.count, chunk, c);
+          buf[j] = reinterpret_cast<const u32x4*>(a.in[d])[send[j] ? (uint64_t)c * cvec + v : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < GP; ++j) {
+          uint8_t* const slot = a.inbox + ((uint64_t)(c0 + j) * N + d) * slot_bytes;
+          if (send[j]) reinterpret_cast<u32x4*>(slot)[v] = buf[j];
+        }
       }
     }
   }
-  // 2. signal: every lane's inbox stores are made visible at agent scope,
-  // then lane c releases semaphore [c][d][b].
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (tail_lane && pc != d)
+    copy_elems<T>(a.in[d], tail_first, a.inbox + ((uint64_t)pc * N + d) * slot_bytes, pv * V,
+                  a.count - tail_first);
+  // 2. signal: once every wave has passed the barrier, lane c stores
+  // semaphore [c][d][b] with agent-scope release.  The barrier orders every
+  // wave's inbox stores before that store, and a release is cumulative, so
+  // one release per semaphore covers the whole workgroup's data.  (An
+  // agent-scope release writes back the XCD's L2 and an acquire invalidates
+  // it; measured on MI355X, an extra release fence in every wave and an
+  // acquire in every wave after the wait cost 8 x 1 MiB f16 29 -> 54 us.)
   __syncthreads();
   if (threadIdx.x < (uint32_t)N && threadIdx.x != d)
     __hip_atomic_store(a.sem + ((uint64_t)threadIdx.x * N + d) * kFlagSlots + b,
                        (uint64_t)F << 32, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 
-  // 3. wait for every peer's slice b (wave 0 polls, one lane per peer)
+  // 3. wait for every peer's slice b: wave 0 polls, one lane per peer, and
+  // acquires; the barrier after it orders the other waves' inbox loads after
+  // that acquire.
   __shared__ int s_ok;
   if (threadIdx.x < 64) {
     const bool mine = threadIdx.x < (uint32_t)N && threadIdx.x != d;
@@ -129,40 +160,37 @@ __global__ void __launch_bounds__(kFmMaxThreads) fullmesh_k(const FullmeshArgs a
     if (threadIdx.x == 0) s_ok = ok ? 1 : 0;
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (s_ok) {
     // reduce slice b of chunk d in rank order and push it to every output
     const uint64_t nd = chunk_elems(a.count, chunk, d);
     const uint8_t* const box = a.inbox + (uint64_t)d * N * slot_bytes;
     for (uint64_t v = v_lo + threadIdx.x; v < v_hi; v += blockDim.x) {
-      const uint64_t first = v * V;
-      if (first >= nd) break;
-      if (first + V <= nd) {
-        float acc[V];
+      if (v * V + V > nd) break;
+      float acc[V];
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        float x[V];
+        if ((uint32_t)s == d) load_vec<T>(a.in[d], (uint64_t)d * cvec + v, x);
+        else load_vec<T>(box + (uint64_t)s * slot_bytes, v, x);
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[j] = round_acc<Acc>(s == 0 ? x[j] : acc[j] + x[j]);
+      }
+      const u32x4 o = encode16<T>(acc);
+#pragma unroll
+      for (int k = 0; k < N; ++k) reinterpret_cast<u32x4*>(a.out[k])[(uint64_t)d * cvec + v] = o;
+    }
+    if (tail_lane && pc == d) {  // the partial vector, element by element
+      for (uint64_t i = tail_first; i < a.count; ++i) {
+        const uint64_t j = i - (uint64_t)d * chunk;
+        float acc = 0.0f;
 #pragma unroll
         for (int s = 0; s < N; ++s) {
-          float x[V];
-          if ((uint32_t)s == d) load_vec<T>(a.in[d], (uint64_t)d * cvec + v, x);
-          else load_vec<T>(box + (uint64_t)s * slot_bytes, v, x);
-#pragma unroll
-          for (int j = 0; j < V; ++j) acc[j] = round_acc<Acc>(s == 0 ? x[j] : acc[j] + x[j]);
+          const float x = (uint32_t)s == d ? load_elem<T>(a.in[d], i)
+                                           : load_elem<T>(box + (uint64_t)s * slot_bytes, j);
+          acc = round_acc<Acc>(s == 0 ? x : acc + x);
         }
-        const u32x4 o = encode16<T>(acc);
 #pragma unroll
-        for (int k = 0; k < N; ++k) reinterpret_cast<u32x4*>(a.out[k])[(uint64_t)d * cvec + v] = o;
-      } else {  // the buffer's last, partial vector: element by element
-        for (uint64_t j = first; j < nd; ++j) {
-          const uint64_t i = (uint64_t)d * chunk + j;
-          float acc = 0.0f;
-#pragma unroll
-          for (int s = 0; s < N; ++s) {
-            const float x = (uint32_t)s == d ? load_elem<T>(a.in[d], i)
-                                             : load_elem<T>(box + (uint64_t)s * slot_bytes, j);
-            acc = round_acc<Acc>(s == 0 ? x : acc + x);
-          }
-#pragma unroll
-          for (int k = 0; k < N; ++k) store_elem<T>(a.out[k], i, acc);
-        }
+        for (int k = 0; k < N; ++k) store_elem<T>(a.out[k], i, acc);
       }
     }
   } else if (threadIdx.x == 0) {
@@ -201,8 +229,8 @@ hipError_t launch_fullmesh(const FullmeshArgs& a, int nranks, int t, int tacc, i
   const dim3 grid((uint32_t)nranks * a.nblocks), block((uint32_t)threads);
 #define MRR_K(N, T, A)                                                          \
   if (nranks == N && t == T && tacc == A) {                                     \
-    hipLaunchKernelGGL((fullmesh_k<N, T, A>), grid, block, 0, stream, a);       \
-    return hipGetLastError();                                                   \
+    return launch_resident((const void*)&fullmesh_k<N, T, A>, grid, block,       \
+    (void*)&a, stream);                                                   \
   }
 #define MRR_ALLN(T, A) MRR_FM_RANKS(MRR_K, T, A)
   MRR_FM_PAIRS(MRR_ALLN)

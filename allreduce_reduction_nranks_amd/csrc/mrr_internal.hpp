@@ -175,5 +175,11 @@ int codec_u_override();
 int codec_wpc_override();
 // False when MRR_RSAG_SMALL=0.
 bool rsag_small_enabled();
+// MRR_COOPERATIVE=1: launch_resident() launches cooperatively.
+bool cooperative_launch_enabled();
+// Launches a kernel whose workgroups wait for each other (one argument block,
+// passed by address): cooperatively when MRR_COOPERATIVE=1, else plainly.
+hipError_t launch_resident(const void* kernel, dim3 grid, dim3 block, void* args,
+                           hipStream_t stream);
 
 }  // namespace mrr

@@ -394,13 +394,13 @@ hipError_t launch_packet_allpair(const PacketArgs& a, int nranks, int t, int tac
   const dim3 grid((uint32_t)nranks * a.nblocks), block((uint32_t)threads);
 #define MRR_K(N, T, A)                                                               \
   if (nranks == N && t == T && tacc == A) {                                          \
-    hipLaunchKernelGGL((packet_allpair_k<N, T, A, 1>), grid, block, 0, stream, a);   \
-    return hipGetLastError();                                                        \
+    return launch_resident((const void*)&packet_allpair_k<N, T, A, 1>, grid, block,   \
+    (void*)&a, stream);                                                        \
   }
 #define MRR_K2(N, T, A)                                                              \
   if (nranks == N && t == T && tacc == A) {                                          \
-    hipLaunchKernelGGL((packet_allpair_k<N, T, A, 2>), grid, block, 0, stream, a);   \
-    return hipGetLastError();                                                        \
+    return launch_resident((const void*)&packet_allpair_k<N, T, A, 2>, grid, block,   \
+    (void*)&a, stream);                                                        \
   }
 #define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
 #define MRR_ALLN2(T, A) MRR_PKT_RANKS_P2(MRR_K2, T, A)
@@ -450,8 +450,8 @@ hipError_t launch_packet_rsag(const PacketRsagArgs& a, int nranks, int t, int ta
   const dim3 grid((uint32_t)nranks * a.nblocks), block((uint32_t)threads);
 #define MRR_K(N, T, A)                                                               \
   if (nranks == N && t == T && tacc == A) {                                          \
-    hipLaunchKernelGGL((packet_rsag_k<N, T, A>), grid, block, 0, stream, a);         \
-    return hipGetLastError();                                                        \
+    return launch_resident((const void*)&packet_rsag_k<N, T, A>, grid, block,         \
+    (void*)&a, stream);                                                        \
   }
 #define MRR_ALLN(T, A) MRR_PKT_RANKS(MRR_K, T, A)
   MRR_PKT_PAIRS(MRR_ALLN)

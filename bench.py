@@ -472,10 +472,12 @@ def bench_rsag(args, torch, mrr, synth):
 
 
 def bench_packet(args, torch, mrr, synth):
-    n, t = 8, "f16"
-    count = args.size * 1024 // 2
+    n, t = args.nranks, args.dtype
+    if n not in (2, 4, 8, 16, 32) or t not in ("f32", "f16", "bf16"):
+        raise SystemExit("c3 takes --nranks 2/4/8/16/32 and --dtype f32/f16/bf16")
+    count = args.size * 1024 // ESIZE[t]
     ins = [x.to("cuda") for x in synth.rank_inputs("uniform", t, n, count, args.seed0)]
-    outs = [torch.empty(count, dtype=torch.float16, device="cuda") for _ in range(n)]
+    outs = [torch.empty_like(x) for x in ins]
     two_phase = args.algo == "rsag"
     fullmesh = args.algo == "fullmesh"
     sbytes = {"allpair": mrr.mrr_packet_scratch_bytes, "rsag": mrr.mrr_packet_rsag_scratch_bytes,
@@ -492,7 +494,7 @@ def bench_packet(args, torch, mrr, synth):
         if st != mrr.MRR_OK:
             raise mrr.MrrError(st)
 
-    S = count * 2
+    S = count * ESIZE[t]
     graph = use_graph(args, n * S)
     eager_us = None
     prime = lambda: poison(outs)  # noqa: E731
@@ -518,7 +520,7 @@ def bench_packet(args, torch, mrr, synth):
         "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall_ms, 5), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic ~U(-1,1)",
-        "config": {"workload": "%s allreduce, 8 ranks x %d KiB f16" % (name, args.size),
+        "config": {"workload": "%s allreduce, %d ranks x %d KiB %s" % (name, n, args.size, t),
                    "nranks": n, "bytes_per_rank": S, "blocks_per_rank": args.blocks,
                    "threads": args.threads, "algorithmic_bytes_per_call": alg_bytes,
                    "algorithmic_gbps": round(alg_bytes / (kern_ms * 1e-3) / 1e9, 2),
@@ -692,8 +694,9 @@ def main():
     ap.add_argument("--dir", default="dec16", choices=sorted(CODEC),
                     help="codec: direction (dec16/dec32 = E4M3B15 -> f16/f32, enc16/enc32 = back)")
     ap.add_argument("--dtype", default="f16", choices=["f32", "f16", "bf16", "fp8", "fp8fn"],
-                    help="custom: type (fp8 = E4M3B15, fp8fn = OCP E4M3FN)")
-    ap.add_argument("--nranks", type=int, default=8, help="c5: rank count")
+                    help="custom / c3: type (fp8 = E4M3B15, fp8fn = OCP E4M3FN; c3 takes "
+                         "f32, f16, bf16)")
+    ap.add_argument("--nranks", type=int, default=8, help="c3 / c5 / custom: rank count")
     ap.add_argument("--out", default="f16", choices=["f16", "fp8", "f32", "dual"],
                     help="c4 / custom FP8: output type (fp8 = the input's FP8 format; c4 dual = "
                          "f16 outputs and the FP8 re-encode from one pass)")

@@ -219,7 +219,9 @@ mrr_status mrr_allreduce_rsag_dual(const void* const* inputs, void* const* outpu
  * other kernel) only delays the packet workgroups that do not fit until it
  * drains.  But two packet calls running at the same time on different
  * streams can each hold workgroups that wait for peers the other keeps off
- * the GPU: order such calls on one stream, or give them a max_spins bound.
+ * the GPU: order such calls on one stream, or give them a max_spins bound,
+ * or set MRR_COOPERATIVE=1 (see mrr_reload_env) to have such launches
+ * refused instead.
  * ------------------------------------------------------------------------ */
 /* Scratch and flag sizes for the calls above; 0 for an unknown type, nranks
  * outside [1, 32], or a count the entry points refuse as too large. */
@@ -438,6 +440,12 @@ size_t mrr_rank_buffer_pitch(size_t bytes_per_rank, int nranks);
  *                      residency (frees the LDS for concurrent kernels)
  *   MRR_RSAG_WPC, MRR_RSAG_ANY_M, MRR_RSAG_SMALL=0, MRR_CODEC_U, MRR_CODEC_WPC
  *                      replace entries of the measured launch tables
+ *   MRR_COOPERATIVE=1  launch the kernels whose workgroups wait for each other
+ *                      (allpair, two-phase packets, full mesh) with
+ *                      hipLaunchCooperativeKernel: a grid that cannot be
+ *                      resident at once (for instance behind work on other
+ *                      streams) is then refused at launch (MRR_EHIP) instead
+ *                      of waiting; costs about 15 us per eager call on MI355X
  * They are read once, when the library is loaded.  mrr_reload_env() reads
  * them again (for tests and tuning sweeps that change them in-process); calls
  * running on other threads meanwhile see either the old or the new values.

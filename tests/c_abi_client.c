@@ -4,12 +4,19 @@
  * count without a compiled kernel, two LL-packet calls on one flag buffer and
  * a refused call, and checks every output against sums computed here.  Data
  * are small integers, so every sum is exact in any order and must match
- * exactly.  Prints "c client ok" and exits 0 on success. */
+ * exactly.  Prints "c client ok" and exits 0 on success.
+ *
+ * With --timing it instead measures small calls from C, without Python in
+ * the way: per call, the host time to issue K calls back to back, and the
+ * GPU time of the same K eager calls between two HIP events on the stream.
+ * One JSON line per call shape. */
+#define _POSIX_C_SOURCE 199309L
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #include "mrr.h"
 
@@ -129,7 +136,107 @@ static int run_packets(void) {
   return bad;
 }
 
-int main(void) {
+/* ---- --timing ------------------------------------------------------------ */
+typedef struct {
+  int kind; /* 0 RS/AG, 1 allpair packets, 2 allpair packets (no-alloc), 3 full mesh */
+  int n;
+  size_t count;
+  mrr_dtype t;
+  void* in[32];
+  void* out[32];
+  void* scratch;
+  size_t sbytes;
+  uint32_t* flags;
+  uint32_t* err;
+} Shape;
+
+static double now_us(void) {
+  struct timespec ts;
+  clock_gettime(CLOCK_MONOTONIC, &ts);
+  return (double)ts.tv_sec * 1e6 + (double)ts.tv_nsec * 1e-3;
+}
+
+static mrr_status issue(Shape* s) {
+  const void* const* in = (const void* const*)s->in;
+  switch (s->kind) {
+    case 0: return mrr_allreduce_rsag(in, s->out, s->count, s->t, s->n, NULL);
+    case 1:
+      return mrr_allreduce_packet(in, s->out, s->scratch, s->sbytes, s->flags, s->count, s->t,
+                                  MRR_F32, s->n, 4000000u, s->err, NULL);
+    case 2:
+      return mrr_allreduce_packet_noalloc(in, s->out, s->count, s->t, MRR_F32, s->n, 4000000u,
+                                          s->err, NULL);
+    default:
+      return mrr_allreduce_fullmesh(in, s->out, s->scratch, s->sbytes, s->flags, s->count, s->t,
+                                    MRR_F32, s->n, 4000000u, s->err, 0, 0, NULL);
+  }
+}
+
+static int time_shape(const char* name, int kind, int n, size_t count, mrr_dtype t, int esize) {
+  Shape s;
+  memset(&s, 0, sizeof(s));
+  s.kind = kind;
+  s.n = n;
+  s.count = count;
+  s.t = t;
+  for (int r = 0; r < n; ++r) {
+    HIP_OK(hipMalloc(&s.in[r], count * esize));
+    HIP_OK(hipMalloc(&s.out[r], count * esize));
+    HIP_OK(hipMemset(s.in[r], 0, count * esize));
+  }
+  if (kind == 1 || kind == 3) {
+    s.sbytes = kind == 1 ? mrr_packet_scratch_bytes(count, t, n) : mrr_fullmesh_scratch_bytes(count, t, n);
+    HIP_OK(hipMalloc(&s.scratch, s.sbytes));
+    HIP_OK(hipMemset(s.scratch, 0, s.sbytes));
+    HIP_OK(hipMalloc((void**)&s.flags, mrr_packet_flag_bytes(n)));
+    HIP_OK(hipMemset(s.flags, 0, mrr_packet_flag_bytes(n)));
+  }
+  HIP_OK(hipMalloc((void**)&s.err, 4));
+  HIP_OK(hipMemset(s.err, 0, 4));
+  const int warm = 50, iters = 2000;
+  for (int i = 0; i < warm; ++i)
+    if (check_status(issue(&s), MRR_OK, name)) return 1;
+  HIP_OK(hipDeviceSynchronize());
+  hipEvent_t e0, e1;
+  HIP_OK(hipEventCreate(&e0));
+  HIP_OK(hipEventCreate(&e1));
+  HIP_OK(hipEventRecord(e0, NULL));
+  const double t0 = now_us();
+  for (int i = 0; i < iters; ++i) issue(&s);
+  const double t1 = now_us();
+  HIP_OK(hipEventRecord(e1, NULL));
+  HIP_OK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  HIP_OK(hipEventElapsedTime(&ms, e0, e1));
+  uint32_t err = 0;
+  HIP_OK(hipMemcpy(&err, s.err, 4, hipMemcpyDeviceToHost));
+  printf("{\"call\": \"%s\", \"nranks\": %d, \"bytes_per_rank\": %zu, \"calls\": %d, "
+         "\"host_issue_us_per_call\": %.3f, \"eager_us_per_call\": %.3f, \"device_error\": %u}\n",
+         name, n, count * esize, iters, (t1 - t0) / iters, ms * 1000.0 / iters, err);
+  HIP_OK(hipEventDestroy(e0));
+  HIP_OK(hipEventDestroy(e1));
+  for (int r = 0; r < n; ++r) {
+    HIP_OK(hipFree(s.in[r]));
+    HIP_OK(hipFree(s.out[r]));
+  }
+  if (s.scratch) HIP_OK(hipFree(s.scratch));
+  if (s.flags) HIP_OK(hipFree(s.flags));
+  HIP_OK(hipFree(s.err));
+  return err != 0;
+}
+
+static int timing(void) {
+  int bad = 0;
+  bad |= time_shape("rsag 2 x 1 MiB bf16", 0, 2, 524288, MRR_BF16, 2);
+  bad |= time_shape("rsag 8 x 16 KiB f16", 0, 8, 8192, MRR_F16, 2);
+  bad |= time_shape("packet allpair 8 x 16 KiB f16", 1, 8, 8192, MRR_F16, 2);
+  bad |= time_shape("packet allpair no-alloc 8 x 16 KiB f16", 2, 8, 8192, MRR_F16, 2);
+  bad |= time_shape("full mesh 8 x 16 KiB f16", 3, 8, 8192, MRR_F16, 2);
+  return bad;
+}
+
+int main(int argc, char** argv) {
+  if (argc > 1 && strcmp(argv[1], "--timing") == 0) return timing();
   int bad = 0;
   bad |= run_f32(8, 100003, 0);  /* compiled kernel */
   bad |= run_f32(3, 50001, 1);   /* runtime-N kernel through the dispatcher */

@@ -23,10 +23,11 @@ ESZ = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "fp8fn": 1}
 
 def blocks_for(n, count, t):
     """An explicit blocks-per-rank choice: one 16-byte vector per lane of a
-    64-lane workgroup, at most 2048 workgroups in all (they all fit at once)."""
+    256-lane workgroup (the default width), at most 512 workgroups in all
+    (they all fit at once)."""
     chunk, _, _ = oracle.default().fullmesh_layout(count, t, n)
     cvec = chunk * ESZ[t] // 16
-    return max(1, min(-(-cvec // 64), 2048 // n, 1024))
+    return max(1, min(-(-cvec // 256), 512 // n, 1024))
 
 
 class State:
