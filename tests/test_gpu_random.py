@@ -1,7 +1,8 @@
 """Randomized differential parity (seeded): a few hundred calls drawn across
 every allreduce entry point -- RS/AG (all chunks or one rank's share, in
 place, element-wise path on unaligned buffers), the size-based dispatcher
-(any rank count 1..32), the allpair and two-phase packet variants, the
+(any rank count 1..32), the allpair and two-phase packet variants and the
+full mesh, the
 one-pass FP8 reduction and the codec -- with random rank counts, sizes
 (weighted toward edges), types and accumulators, each compared bit for bit
 with the CPU oracle.  Every case prints its parameters before it runs."""
@@ -111,17 +112,19 @@ def test_random_packets(case):
     rng = np.random.default_rng(50_000 + case)
     n = int(rng.choice(COMPILED))
     t, acc = PKT_PAIRS[int(rng.integers(len(PKT_PAIRS)))]
-    two_phase = bool(rng.random() < 0.5)
+    algo = ["allpair", "two-phase", "fullmesh"][min(2, int(rng.random() * 3))]
     count = max(1, rand_count(rng, 20_000 // n + 64))
     calls = int(rng.integers(1, 4))
-    announce("random packets", case, n, t, acc, count, "two-phase" if two_phase else "allpair", calls)
-    size_fn = mrr.mrr_packet_rsag_scratch_bytes if two_phase else mrr.mrr_packet_scratch_bytes
+    announce("random packets", case, n, t, acc, count, algo, calls)
+    size_fn = {"allpair": mrr.mrr_packet_scratch_bytes, "two-phase": mrr.mrr_packet_rsag_scratch_bytes,
+               "fullmesh": mrr.mrr_fullmesh_scratch_bytes}[algo]
     sbytes = max(8, size_fn(count, t, n))
     scratch = torch.zeros(sbytes // 8 + 1, dtype=torch.int64, device="cuda")
     flags = torch.zeros(n * mrr.PKT_FLAG_SLOTS, dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     outs = [empty_bytes(t, count, 0x5A) for _ in range(n)]
-    entry = mrr.mrr_allreduce_packet_rsag if two_phase else mrr.mrr_allreduce_packet_ex
+    entry = {"allpair": mrr.mrr_allreduce_packet_ex, "two-phase": mrr.mrr_allreduce_packet_rsag,
+             "fullmesh": mrr.mrr_allreduce_fullmesh}[algo]
     for call in range(calls):
         ins = inputs_for(t, n, count, seed0=60_000 + 97 * case + 7 * call, kind=kind_for(t))
         st = entry(ins, outs, scratch, sbytes, flags, count, t, acc, n, 2_000_000, err)
