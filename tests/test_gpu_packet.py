@@ -302,3 +302,20 @@ def test_flag_buffer_save_restore_and_recycle():
     copies = [x.clone() for x in ins]
     assert allpair(ins, outs, fresh, t, "f32") == mrr.MRR_OK
     check_call(ins, outs, fresh, t, "f32", 1, copies, "recycled")
+
+
+def test_flag_wrap_skips_zero():
+    """Flag slots preset near the top of the 32-bit range (scratch zeroed):
+    the calls stamp 2^32 - 1 and then 1, skipping 0, and every output,
+    scratch packet and flag slot is the oracle's -- the documented wrap, on
+    a buffer re-zeroed as the wrap contract asks."""
+    n, t, count = 4, "bf16", 5000
+    announce("packet flag wrap")
+    st = PacketState(n, count, t)
+    st.flags.fill_(-2)  # every slot 0xFFFFFFFE
+    outs = [empty(t, count, 0xEE) for _ in range(n)]
+    for flag in (0xFFFFFFFF, 1, 2):
+        ins = inputs_for(t, n, count, seed0=4300 + (flag & 0xFF), kind="uniform")
+        copies = [x.clone() for x in ins]
+        assert allpair(ins, outs, st, t, "f32") == mrr.MRR_OK
+        check_call(ins, outs, st, t, "f32", flag, copies, "flag %#x" % flag)

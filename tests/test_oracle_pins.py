@@ -489,6 +489,23 @@ def test_next_flag(orc):
     assert orc.next_flag(0) == 1 and orc.next_flag(5) == 6 and orc.next_flag(0xFFFFFFFF) == 1
 
 
+def test_flag_sequence_wraps_past_zero(orc):
+    """The flag a call stamps is one more than the slots hold and never 0 (0
+    marks a slot no call has written): across the 32-bit wrap the sequence
+    runs ..., 2^32 - 2, 2^32 - 1, 1, 2, ..., so it repeats every 2^32 - 1
+    calls -- the period after which stale packets could carry a current
+    flag again, which is why the flag buffer and scratch are re-zeroed before
+    then."""
+    seq, f = [], 0xFFFFFFFC
+    for _ in range(5):
+        f = orc.next_flag(f)
+        seq.append(f)
+    assert seq == [0xFFFFFFFD, 0xFFFFFFFE, 0xFFFFFFFF, 1, 2]
+    # a packet stamped just after the wrap carries flag 1 in its high word
+    pk = orc.pack(np.arange(8, dtype=np.uint8), orc.next_flag(0xFFFFFFFF))
+    assert np.all((pk >> np.uint64(32)) == 1)
+
+
 @pytest.mark.parametrize("t,count", [("f16", 1001), ("f32", 64), ("bf16", 7), ("fp8", 1023)])
 def test_allreduce_packet_expectation(orc, t, count):
     nranks = 4
