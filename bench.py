@@ -109,6 +109,24 @@ class Timer:
         kern_ms = e0.elapsed_time(e1) / steps
         return wall_ms, kern_ms
 
+    def per_call(self, fn, steps):
+        """K more calls with an event between consecutive calls: the per-call
+        durations' median, min and max in us (a pass of its own, so the
+        extra events do not touch the mean above)."""
+        import statistics
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(steps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        d = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+        return {"median": round(statistics.median(d), 2), "min": round(min(d), 2),
+                "max": round(max(d), 2), "calls": steps}
+
     def run_graph(self, fn, steps, warmup, prime=None):
         """The K calls captured once into a HIP graph and replayed: per-call
         GPU time without the host's per-call launch cost (what a captured
@@ -407,10 +425,25 @@ def bench_rsag(args, torch, mrr, synth):
         wall_ms, kern_ms = Timer(torch).run_graph(step, args.steps, args.warmup, prime)
     else:
         wall_ms, kern_ms = Timer(torch).run(step, args.steps, args.warmup, prime)
-    # Nothing below writes `outs` again (the layout comparison and the copy
-    # ceiling use buffers of their own): the parity check reads what the last
-    # timed call wrote.
+    # The parity check reads what the last timed call wrote, so the per-call
+    # pass below writes other buffers of the same layout, and nothing else
+    # here writes `outs` (the layout comparison and the copy ceiling use
+    # buffers of their own).
     checked = outs
+    per_call = None
+    if not graph:
+        if args.layout == "pitch":  # the timed outputs' placement
+            _, spare = mrr.alloc_rank_buffers(n, count, tout)
+        else:
+            spare = [torch.empty_like(o) for o in outs]
+
+        def step_spare():
+            st = mrr.mrr_allreduce_rsag_ex(ins, spare, count, t, acc, tout, n, rank) \
+                if compiled else mrr.mrr_allreduce(ins, spare, count, t, acc, n)
+            if st != mrr.MRR_OK:
+                raise mrr.MrrError(st)
+        per_call = Timer(torch).per_call(step_spare, args.steps)
+        del spare
     sep_us = None
     if args.layout == "pitch" and args.layout_compare:
         def step_sep():
@@ -453,6 +486,8 @@ def bench_rsag(args, torch, mrr, synth):
     add_ceilings(result, ceiling, achieved)
     if sep_us is not None:
         result["config"]["kernel_us_one_allocation_per_rank"] = round(sep_us, 2)
+    if per_call is not None:
+        result["config"]["kernel_us_per_call"] = per_call
     result["config"]["timing"] = TIMING_GRAPH if graph else TIMING_EAGER
     if eager_us is not None:
         result["config"]["eager_us_per_call"] = round(eager_us, 2)

@@ -85,6 +85,39 @@ def test_parity_compiled_kernel_sizes(n, t, acc, tout):
     check_all(outs, want, tout, "n=%d %s/%s/%s" % (n, t, acc, tout))
 
 
+# FP8 inputs to f32 outputs run a kernel of their own at most rank counts
+# (16 codes per lane, stores transposed through LDS).  count = N (1024 m + 512)
+# - 1000: from 4 ranks up every chunk is m whole 1024-element tiles and a half
+# tile, and the last chunk is 1000 elements short, so its last tile is partial
+# (33 of 64 lanes store), the tile after it starts past the buffer's last whole
+# 16-element unit, and 8 elements form the scalar tail (2 ranks: chunks of
+# 1024 m + 256, the last one 16 lanes into its last tile plus the same tail).
+# m keeps N <= 8 well above the small-call switch, so the compiled kernels run.
+WIDE_CASES = [(n, t, acc) for n in (2, 4, 8, 16, 32) for t in ("fp8", "fp8fn")
+              for acc in ("f32", "f16", t)]
+
+
+@pytest.mark.parametrize("n,t,acc", WIDE_CASES, ids=["%d-%s-%s" % c for c in WIDE_CASES])
+def test_parity_fp8_to_f32_tiles(n, t, acc):
+    m = {2: 2048, 4: 2048, 8: 512}.get(n, 16)
+    count = n * (1024 * m + 512) - 1000
+    per = -(-count // n)
+    chunk = -(-per // CHUNK_ALIGN[t]) * CHUNK_ALIGN[t]
+    announce("rsag fp8 -> f32 tiles", n, t, acc, count)
+    ins = inputs_for(t, n, count, seed0=700 + n)
+    host = [bits(x) for x in ins]
+    want = oracle_allreduce_threaded(host, t, acc, "f32")
+    check_all(run(ins, t, acc, "f32"), want, "f32", "n=%d %s/%s" % (n, t, acc))
+    # The last rank's share alone: its chunk is the short one.
+    r = n - 1
+    outs = run(ins, t, acc, "f32", rank=r, fill=0x5A)
+    lo = r * chunk
+    for k, o in enumerate(outs):
+        b = bits(o)
+        assert_bits_equal(b[lo:], want[lo:], "f32", "rank %d out %d" % (r, k))
+        assert np.all(b[:lo].view(np.uint8) == 0x5A), "rank %d wrote outside its chunk" % r
+
+
 @pytest.mark.parametrize("t", ["f32", "f16", "bf16", "fp8"])
 @pytest.mark.parametrize("count", [1, 3, 7, 8, 9, 15, 16, 17, 31, 33, 127, 129, 4095, 4097])
 def test_edge_counts(t, count):
