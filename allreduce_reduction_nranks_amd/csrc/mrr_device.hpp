@@ -301,20 +301,12 @@ __device__ __forceinline__ void decode_word_fp8_hw(uint32_t w, float* x) {
   x[3] = hi.y;
 }
 
-// True when any byte of the word has exponent field 15.
-__device__ __forceinline__ bool fp8_word_has_e15(uint32_t w) {
-  const uint32_t t = (w & 0x78787878u) ^ 0x78787878u;  // zero byte <=> e == 15
-  return ((t - 0x01010101u) & ~t & 0x80808080u) != 0;
-}
-
-// Replaces the values of exponent-15 codes of one word by inf or NaN.
-__device__ __forceinline__ void fix_fp8_e15_word(uint32_t w, float* x) {
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const uint32_t c = (w >> (8 * b)) & 0xFFu;
-    if ((c & 0x78u) == 0x78u) x[b] = fp8_to_f32(c);
-  }
-}
+// Bit 7 of byte b of the result is set exactly when byte b of w has
+// exponent field 15 (inf or NaN in E4M3B15): (b & 0x78) + 8 reaches 0x80 only
+// from 0x78, and no byte carries into the next.  The marks of many words are
+// OR-ed together and tested once against kFp8E15Bits.
+__device__ __forceinline__ uint32_t fp8_e15_marks(uint32_t w) { return (w & 0x78787878u) + 0x08080808u; }
+constexpr uint32_t kFp8E15Bits = 0x80808080u;
 
 // ---------------------------------------------------------------------------
 // 16-byte vector decode / encode.  An input vector holds VW = 16 / size(In)

@@ -58,23 +58,31 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup (all kernels but one
 //                             N=8 0.81 (f16) / 0.77, N=16 0.78 / 0.76,
 //                             N=32 0.75 / 0.77; with groups of 16 ranks at 8
 //                             per CU, N=32 ran 0.70 / 0.70)
-//   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: FP8 out U=1 x8 (E4M3FN out x6),
-//                             f16 out U=1 x6, f32 out U=2 (128-lane tiles,
-//                             below) x4 (E4M3FN x2) -- f32 outputs at most
-//                             rank counts take rsag_wide_f32_kernel instead
-//                             (rsag_wide_wg_per_cu);
+//   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: U=1 for FP8 and f16 outputs,
+//                             U=2 (128-lane tiles, below) x2 for f32 outputs,
+//                             which at most rank counts take
+//                             rsag_wide_f32_kernel instead (rsag_wide_wg_per_cu);
 //                             N=2: U=4 times 2 for f16 and 4 for f32 outputs
-//                             (a lane loads 16 bytes per rank); workgroups per
-//                             CU (2-8 swept at 32 MiB per rank) E4M3B15: 8 for
-//                             FP8 out, 6 for f16, 8 for f32; E4M3FN: 8 for FP8
-//                             out, 4 for f16, 2 for f32.
+//                             (a lane loads 16 bytes per rank).  Workgroups per
+//                             CU, swept 4-16 at 32 MiB per rank (fractions of
+//                             the HBM peak at the chosen cap, E4M3B15 /
+//                             E4M3FN):
+//                               FP8 out: N=2 x16 (0.74 / 0.73), N=4 x12 / x8
+//                                 (0.75 / 0.77), N=8 x6 (0.81 / 0.78),
+//                                 N=16 x6 (0.76 / 0.77), N=32 x4 (0.74 / 0.73);
+//                               f16 out: N=2 x4 (0.74 / 0.75), N=4 x16 / x8
+//                                 (0.74 / 0.77), N=8 x6 (0.80 / 0.80),
+//                                 N=16 x4 (0.74 / 0.75), N=32 x6 (0.71 / 0.71).
+//                             At 4 ranks fewer than 8 workgroups per CU starve
+//                             the memory system (E4M3B15 -> f16 0.39 at 4,
+//                             0.59 at 8).
 //   One-pass FP8 -> f16 + FP8 (rsag_dual_kernel): U=2 x4 (U=8 x4 at N=2; 2-8
 //                             swept at 8 x 32 MiB and 2 x 32 MiB).
 //   Workgroup width: 64 lanes, except FP8 inputs with f32 outputs above two
-//   ranks, which run two-wave (128-lane) tiles at 4 (E4M3B15) or 2 (E4M3FN)
-//   workgroups per CU: 8 x 32 MiB E4M3B15 0.69 -> 0.72 of the HBM peak,
-//   E4M3FN 0.68 -> 0.75.  Wider tiles lost elsewhere (FP8 and one-pass
-//   outputs, 16-bit data at 2, 8 and 32 ranks).
+//   ranks, which run two-wave (128-lane) tiles at 2 workgroups per CU:
+//   8 x 32 MiB E4M3B15 0.69 -> 0.74 of the HBM peak, E4M3FN 0.68 -> 0.75.
+//   Wider tiles lost elsewhere (FP8 and one-pass outputs, 16-bit data at 2,
+//   8 and 32 ranks).
 constexpr int rsag_threads(int n, int tin, int tout) {
   return is_fp8(tin) && tout == kF32 && n > 2 ? 128 : kRsagThreads;
 }
@@ -87,12 +95,16 @@ constexpr int rsag_unroll(int n, int tin, int tout) {
 }
 constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
   if (is_fp8(tin)) {
-    if (n == 2) {
-      if (tin == kFP8FN) return tout == kF32 ? 2 : tout == kF16 ? 4 : 8;
-      return tout == kF16 ? 6 : 8;
+    const bool fn = tin == kFP8FN;
+    const bool f16 = tout == kF16;
+    if (tout == kF32) return n == 2 && !fn ? 8 : 2;  // 128-lane workgroups above 2 ranks
+    switch (n) {
+      case 2: return f16 ? 4 : 16;
+      case 4: return fn ? 8 : f16 ? 16 : 12;
+      case 16: return f16 ? 4 : 6;
+      case 32: return f16 ? 6 : 4;
+      default: return 6;
     }
-    if (tout == kF32) return tin == kFP8FN ? 2 : 4;  // 128-lane workgroups
-    return tout == kFP8 ? 8 : 6;
   }
   return n == 2 ? 12 : n == 4 ? 8 : n == 8 ? 8 : 4;
 }
@@ -140,6 +152,28 @@ template <int In, int Out> struct Unit {
   static constexpr int EPW = 4 / Ty<In>::size;  // elements per input word
 };
 
+// E4M3B15 units holding an exponent-15 code (inf / NaN) are reduced again
+// here, from memory: the exact decode, every partial sum rounded exactly to
+// Acc (the hardware converts the fast path uses are exact for finite data
+// only).  unit indexes D-word units of every input.
+template <int D, int Acc>
+__device__ __forceinline__ void fp8_unit_exact(const void* const* in, int n, uint64_t unit,
+                                               float* acc) {
+#pragma unroll 1
+  for (int r = 0; r < n; ++r) {
+    uint32_t w[D];
+    ld_words<D>(in[r], unit, w);
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float x = fp8_to_f32((w[j] >> (8 * b)) & 0xFFu);
+        acc[4 * j + b] = round_acc<Acc>(r == 0 ? x : acc[4 * j + b] + x);
+      }
+    }
+  }
+}
+
 // Reduces UU units v0 + u * T (u < UU; T lanes per workgroup) over the N ranks and stores
 // each result to all N outputs.  The first partial sum is x_0 rounded to the
 // accumulator type (the identity except for an FP8 accumulator, which
@@ -147,10 +181,11 @@ template <int In, int Out> struct Unit {
 // of G: the group's UU * G loads are all issued before the first add of the
 // group, then the adds run in rank order.
 //
-// FP8 inputs decode through the hardware E4M3 converts; a lane whose words
-// hold an exponent-15 code (inf / NaN) marks that unit `special`, fixes
-// those values, and rounds / encodes that unit with the exact bit arithmetic
-// instead of the converts, which are only exact for finite data.
+// FP8 inputs decode through the hardware E4M3 converts.  For E4M3B15 every
+// loaded word also adds to the unit's exponent-15 marks; a unit that holds an
+// exponent-15 code (inf / NaN) is `special`: after the rank loop it is
+// reduced again by fp8_unit_exact and encoded with the exact bit arithmetic.
+// One branch per unit, taken only for such data.
 //
 // Out2 != 0 (FP8 types only, with Out = f16): each unit's 8 sums are also
 // encoded to Out2 and stored, 8 bytes per lane, to out2[0..N-1].
@@ -163,8 +198,9 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
   static_assert(N % G == 0, "rank group must divide N");
   float acc[UU][UE];
   bool special[UU];
+  uint32_t marks[UU];
 #pragma unroll
-  for (int u = 0; u < UU; ++u) special[u] = false;
+  for (int u = 0; u < UU; ++u) marks[u] = 0;
   constexpr int kGroupUnroll = N / G <= 2 ? N / G : 1;
 #pragma unroll kGroupUnroll
   for (int g = 0; g < N; g += G) {
@@ -183,10 +219,7 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
         for (int j = 0; j < D; ++j) {
           if constexpr (In == kFP8) {
             decode_word_fp8_hw(raw[u][r][j], x + j * EPW);
-            if (fp8_word_has_e15(raw[u][r][j])) {
-              fix_fp8_e15_word(raw[u][r][j], x + j * EPW);
-              special[u] = true;
-            }
+            marks[u] |= fp8_e15_marks(raw[u][r][j]);
           } else {
             decode_word<In>(raw[u][r][j], x + j * EPW);
           }
@@ -194,10 +227,17 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
 #pragma unroll
         for (int j = 0; j < UE; ++j) {
           const float s = g + r == 0 ? x[j] : acc[u][j] + x[j];
-          if constexpr (Acc == kFP8) acc[u][j] = special[u] ? round_acc<kFP8>(s) : round_fp8_hw(s);
+          if constexpr (Acc == kFP8) acc[u][j] = round_fp8_hw(s);
           else acc[u][j] = round_acc<Acc>(s);
         }
       }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UU; ++u) {
+    special[u] = (marks[u] & kFp8E15Bits) != 0u;
+    if constexpr (In == kFP8) {
+      if (special[u]) fp8_unit_exact<D, Acc>(a.in, N, v0 + (uint64_t)u * T, acc[u]);
     }
   }
   // Store order: at 16 ranks each workgroup starts its N stores at output
@@ -293,7 +333,7 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_wide_f32_kernel(const RsagA
     // Lanes past the end load unit u_base instead (in range), so no load waits on a branch.
     const uint64_t u = u_base + lane < v_hi ? u_base + lane : u_base;
     float acc[kWideUE];
-    bool special = false;
+    uint32_t marks = 0;
 #pragma unroll 1
     for (int g = 0; g < N; g += G) {
       u32x4 raw[G];
@@ -307,10 +347,7 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_wide_f32_kernel(const RsagA
           const uint32_t w = raw[r][j];
           if constexpr (In == kFP8) {
             decode_word_fp8_hw(w, x + 4 * j);
-            if (fp8_word_has_e15(w)) {
-              fix_fp8_e15_word(w, x + 4 * j);
-              special = true;
-            }
+            marks |= fp8_e15_marks(w);
           } else {
             decode_word<In>(w, x + 4 * j);
           }
@@ -318,10 +355,13 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_wide_f32_kernel(const RsagA
 #pragma unroll
         for (int j = 0; j < kWideUE; ++j) {
           const float s = g + r == 0 ? x[j] : acc[j] + x[j];
-          if constexpr (Acc == kFP8) acc[j] = special ? round_acc<kFP8>(s) : round_fp8_hw(s);
+          if constexpr (Acc == kFP8) acc[j] = round_fp8_hw(s);
           else acc[j] = round_acc<Acc>(s);
         }
       }
+    }
+    if constexpr (In == kFP8) {
+      if ((marks & kFp8E15Bits) != 0u) fp8_unit_exact<4, Acc>(a.in, N, u, acc);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -363,8 +403,9 @@ __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint6
   constexpr int EPW = Unit<In, Out>::EPW;
   float acc[UU][UE];
   bool special[UU];
+  uint32_t marks[UU];
 #pragma unroll
-  for (int u = 0; u < UU; ++u) special[u] = false;
+  for (int u = 0; u < UU; ++u) marks[u] = 0;
   for (int g = 0; g < n; g += G) {
     uint32_t raw[UU][G][D];
 #pragma unroll
@@ -383,10 +424,7 @@ __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint6
         for (int j = 0; j < D; ++j) {
           if constexpr (In == kFP8) {
             decode_word_fp8_hw(raw[u][r][j], x + j * EPW);
-            if (fp8_word_has_e15(raw[u][r][j])) {
-              fix_fp8_e15_word(raw[u][r][j], x + j * EPW);
-              special[u] = true;
-            }
+            marks[u] |= fp8_e15_marks(raw[u][r][j]);
           } else {
             decode_word<In>(raw[u][r][j], x + j * EPW);
           }
@@ -394,10 +432,17 @@ __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint6
 #pragma unroll
         for (int j = 0; j < UE; ++j) {
           const float s = g + r == 0 ? x[j] : acc[u][j] + x[j];
-          if constexpr (Acc == kFP8) acc[u][j] = special[u] ? round_acc<kFP8>(s) : round_fp8_hw(s);
+          if constexpr (Acc == kFP8) acc[u][j] = round_fp8_hw(s);
           else acc[u][j] = round_acc<Acc>(s);
         }
       }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UU; ++u) {
+    special[u] = (marks[u] & kFp8E15Bits) != 0u;
+    if constexpr (In == kFP8) {
+      if (special[u]) fp8_unit_exact<D, Acc>(a.in, n, v0 + (uint64_t)u * kRsagThreads, acc[u]);
     }
   }
 #pragma unroll
@@ -553,17 +598,16 @@ static void launch_vec_typed(int nranks, const RsagShape& sh, const RsagArgs& a,
 // (3 ranks 0.81 of the HBM peak; the persistent-grid table, M=4 at 12 per
 // CU, gave 0.76), 8 per CU for N <= 8 (5, 6, 7 ranks 0.81, 0.80, 0.80,
 // against 0.74-0.77 at M=2 and 4 per CU), 4 per CU above (12 x f16 0.78,
-// 24 x bf16 0.73).  FP8 inputs keep M=1, at 12 workgroups per CU for E4M3B15
-// (its decode checks each word for exponent-15 codes; 6 and 12 ranks to
-// E4M3B15 0.70 / 0.71, against 0.52 / 0.55 at 6 per CU) and 8 for E4M3FN
-// (0.74 / 0.74, against 0.70 / 0.75).
+// 24 x bf16 0.73).  FP8 inputs keep M=1, at 8 workgroups per CU (6, 12 and
+// 24 ranks to E4M3B15 0.72 / 0.74 / 0.72, against 0.72 / 0.74 / 0.70 at 12
+// per CU; E4M3FN 0.74 / 0.74 at 6 and 12 ranks).
 // MRR_RSAG_ANY_M and MRR_RSAG_WPC override.
 constexpr int rsag_any_unroll(int tin, int tout) {
   return is_fp8(tin) ? (tout == kF32 ? 4 : tout == kF16 ? 2 : 1) : 1;
 }
 static int rsag_any_multiplier(int) { return 1; }
 static int rsag_any_wg_per_cu(int n, int tin) {
-  if (is_fp8(tin)) return tin == kFP8FN ? 8 : 12;
+  if (is_fp8(tin)) return 8;
   return n <= 4 ? 16 : n <= 8 ? 8 : 4;
 }
 template <int In, int Acc, int Out>
