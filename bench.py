@@ -292,11 +292,11 @@ _NAN_TEST = {  # bit pattern -> NaN, on integer views of the element type
 def count_mismatches(torch, outs, want_bits, t, lo=0):
     """Elements of outs[k][lo : lo + len(want_bits)] whose bits differ from
     the oracle's (NaN against NaN counts as equal: only NaN-ness is
-    specified), summed over every output k; compared on the GPU."""
+    specified), summed over every output k; compared on the outputs' device."""
     import numpy as np
     e = ESIZE[t]
     ints = {1: (np.uint8, torch.uint8), 2: (np.int16, torch.int16), 4: (np.int32, torch.int32)}[e]
-    want = torch.from_numpy(np.ascontiguousarray(want_bits).view(ints[0])).to("cuda")
+    want = torch.from_numpy(np.ascontiguousarray(want_bits).view(ints[0])).to(outs[0].device)
     n = want.numel()
     bad = 0
     for o in outs:
