@@ -116,6 +116,8 @@ constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
 //            (x4, a tie: kept general), N=16 0.69 -> 0.70 (x2), N=32 0.63 -> 0.66 (x2);
 //   E4M3FN:  N=2 0.76 -> 0.75 (kept general), N=4 0.62 -> 0.73 (x6), N=8 0.74 -> 0.71
 //            (kept general), N=16 0.69 -> 0.71 (x2), N=32 0.65 -> 0.67 (x2).
+// With the one-branch exponent-15 check the general kernel at 8 ranks runs
+// 0.74 for both formats at 2 per CU, against 0.71 for this one.
 constexpr int rsag_wide_wg_per_cu(int n, int tin) {
   return n == 2 ? (tin == kFP8 ? 12 : 0) : n == 4 ? 6 : (n == 16 || n == 32) ? 2 : 0;
 }
@@ -389,12 +391,17 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_wide_f32_kernel(const RsagA
 }
 
 // Runtime rank count (1..32): the fallback for counts without a compiled
-// kernel.  Ranks are taken in groups of G (8 up to 8 ranks or with FP8 data or
-// accumulator, else 16) behind
-// wavefront-uniform bounds, in rank order, with the same unit structure as
-// reduce_store: all loads of a group are issued before its first add.
+// kernel.  Ranks are taken in groups of G behind wavefront-uniform bounds, in
+// rank order, with the same unit structure as reduce_store: all loads of a
+// group are issued before its first add.  G is 16 for 9 to 20 ranks of 16- or
+// 32-bit data and 8 otherwise (FP8 data or accumulator, up to 8 ranks, above
+// 20 ranks).  Measured on MI355X, 64 MiB of bf16 per rank at 4 workgroups
+// per CU, groups of 16 -> 8: 24 ranks 0.727 -> 0.748, 28 ranks 0.713 ->
+// 0.733, 31 ranks 0.699 -> 0.721; at 12 and 20 ranks groups of 8 were
+// 1-2 % slower in an earlier session and equal in this one.
 constexpr int kAnyGroup = 8;
 constexpr int kAnyGroupWide = 16;
+constexpr int kAnyGroupWideMaxRanks = 20;
 
 template <int In, int Acc, int Out, int UU, int G>
 __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint64_t v0) {
@@ -620,7 +627,7 @@ static void launch_any_typed(int n, int mult, const RsagShape& sh, const RsagArg
   // FP8 data or accumulators keep groups of 8 (as the compiled kernels do):
   // their per-rank decode state for 16 ranks no longer stays in registers.
   constexpr bool wide_ok = !is_fp8(In) && !is_fp8(Acc);
-  if (wide_ok && n > kAnyGroup) {
+  if (wide_ok && n > kAnyGroup && n <= kAnyGroupWideMaxRanks) {
     hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, wide_ok ? kAnyGroupWide : kAnyGroup>), grid,
                        block, lds, s, a);
   } else if constexpr (is_fp8(In)) {
