@@ -118,6 +118,48 @@ def test_parity_fp8_to_f32_tiles(n, t, acc):
         assert np.all(b[:lo].view(np.uint8) == 0x5A), "rank %d wrote outside its chunk" % r
 
 
+def plant_fp8_specials(ins, t, seed):
+    """Every exponent-15 code of E4M3B15 (inf, NaN) or the NaNs and largest
+    finite values of E4M3FN, signed zeros and the smallest subnormals, at
+    1/64 of the positions of each rank."""
+    rng = np.random.default_rng(seed)
+    special = np.array(list(range(0x78, 0x80)) + list(range(0xF8, 0x100)) + [0x00, 0x80, 0x01, 0x81]
+                       if t == "fp8" else [0x7F, 0xFF, 0x7E, 0xFE, 0x00, 0x80, 0x01, 0x81], np.uint8)
+    out = []
+    for x in ins:
+        h = bits(x).copy()
+        pos = rng.integers(0, h.size, max(1, h.size // 64))
+        h[pos] = rng.choice(special, pos.size)
+        out.append(torch.from_numpy(h).cuda())
+    return out
+
+
+# FP8 inputs holding inf / NaN codes at sizes that run the compiled kernels
+# (the general kernel, the 16-codes-per-lane kernel for f32 outputs) and the
+# runtime-N kernel well above the small-call switch: a unit holding such a
+# code is reduced again with the exact decode, so this covers that path in
+# every kernel, every output type and every accumulator.
+SPECIAL_CASES = [(n, t, acc, o) for n in (2, 4, 8, 16, 32) for t in ("fp8", "fp8fn")
+                 for acc in ("f32", "f16", t) for o in (t, "f16", "f32")] + \
+                [(n, t, acc, t) for n in (3, 12) for t in ("fp8", "fp8fn") for acc in ("f32", "f16", t)]
+
+
+@pytest.mark.parametrize("n,t,acc,tout", SPECIAL_CASES, ids=["%d-%s-%s-%s" % c for c in SPECIAL_CASES])
+def test_fp8_special_codes_at_kernel_sizes(n, t, acc, tout):
+    # 2 ranks: over 512 tiles of 4096 codes, above the small-call switch
+    count = (1 << 21) + (1 << 16) + 1031 if n == 2 else (600 * 1024 + 7 if n <= 12 else n * 16896 - 1000)
+    announce("rsag fp8 specials", n, t, acc, tout, count)
+    ins = plant_fp8_specials(inputs_for(t, n, count, seed0=1300 + n), t, seed=n)
+    if n in (2, 4, 8, 16, 32):
+        outs = run(ins, t, acc, tout)
+    else:
+        outs = [empty(tout, count, 0xA5) for _ in range(n)]
+        assert mrr.mrr_allreduce(ins, outs, count, t, acc, n) == mrr.MRR_OK
+        torch.cuda.synchronize()
+    want = oracle.allreduce([bits(x) for x in ins], t, acc, tout)
+    check_all(outs, want, tout, "specials n=%d %s/%s/%s" % (n, t, acc, tout))
+
+
 @pytest.mark.parametrize("t", ["f32", "f16", "bf16", "fp8"])
 @pytest.mark.parametrize("count", [1, 3, 7, 8, 9, 15, 16, 17, 31, 33, 127, 129, 4095, 4097])
 def test_edge_counts(t, count):
