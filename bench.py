@@ -442,7 +442,8 @@ def bench_rsag(args, torch, mrr, synth):
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     key = {"c1": "rsag_2x1MiB_bf16", "c2": "rsag_8x64MiB_f16",
            "c4": "rsag_8x32MiB_%s_to_%s" % (t, tout), "c5": "rsag_%dx256MiB_bf16" % n,
-           "custom": "rsag_%dx%dKiB_%s" % (n, args.size, t)}[args.config]
+           "custom": "rsag_%dx%dKiB_%s%s" % (n, args.size, t,
+                                              "" if tout == t else "_to_" + tout)}[args.config]
     traffic = measured_traffic(key)
     ceiling = copy_ceiling(torch, mrr, n * count * ESIZE[t]) if args.copy_ceiling else None
     workload = {"c1": "RS/AG allreduce, 2 ranks x 1 MiB bf16 ~N(0,1), fp32 accumulation",

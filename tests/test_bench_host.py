@@ -107,6 +107,7 @@ def test_committed_summaries_match_the_current_sources():
     the kernel sources as they stand, so the bench line's traffic is set."""
     keys = {"rsag_8x64MiB_f16": None, "rsag_16x256MiB_bf16": None, "rsag_32x256MiB_bf16": None,
             "rsag_8x32MiB_fp8fn_to_fp8fn": None, "rsag_dual_8x32MiB_fp8": None,
+            "rsag_16x32768KiB_fp8_to_f32": None,
             "codec_dec16_256Mi": bench.CODEC_SOURCES, "codec_enc32_256Mi": bench.CODEC_SOURCES}
     for key, src in keys.items():
         t = bench.measured_traffic(key, src)
