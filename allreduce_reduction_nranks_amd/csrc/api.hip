@@ -262,11 +262,20 @@ int mrr_version(void) { return 10100; }
 
 void mrr_reload_env(void) { read_env(); }
 
+// From 4 ranks up, buffers an odd multiple of 128 MiB long take another
+// stagger: at the usual one their equal-offset streams collide (measured on
+// MI355X, bf16 RS/AG, fractions of the HBM peak, usual stagger -> this one:
+// 8 ranks x 128 MiB 0.74 -> 0.80, x 384 MiB 0.77 -> 0.80; 4 x 128 MiB 0.77 ->
+// 0.80; 32 x 128 MiB 0.70 -> 0.74; 16 x 128 MiB unchanged at 0.77; 2 x 128
+// MiB is fine at 4 KiB, 0.80, and slower at 5 KiB, 0.78).  Sizes 64, 96, 160,
+// 192, 256, 320 and 512 MiB keep the usual stagger, as good or better there.
 size_t mrr_rank_buffer_pitch(size_t bytes_per_rank, int nranks) {
   if (bytes_per_rank == 0 || nranks < 1) return 0;
   const size_t page = 4096;
-  const size_t stagger = nranks >= 16 ? 3072 : 4096;
-  return (bytes_per_rank + page - 1) / page * page + stagger;
+  const size_t rounded = (bytes_per_rank + page - 1) / page * page;
+  const bool odd128 = nranks >= 4 && rounded % ((size_t)256 << 20) == ((size_t)128 << 20);
+  const size_t stagger = nranks >= 16 ? (odd128 ? 8192 : 3072) : (odd128 ? 5120 : 4096);
+  return rounded + stagger;
 }
 
 // Shared by mrr_allreduce_rsag_ex (compiled rank counts only, as the RS/AG

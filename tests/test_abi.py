@@ -209,10 +209,18 @@ def test_rank_buffer_pitch(lib):
     assert mrr.mrr_rank_buffer_pitch(64 * MiB, 8) == 64 * MiB + 4096
     assert mrr.mrr_rank_buffer_pitch(64 * MiB, 16) == 64 * MiB + 3072
     assert mrr.mrr_rank_buffer_pitch(64 * MiB + 1, 2) == 64 * MiB + 8192
+    # odd multiples of 128 MiB take the other stagger; even ones and others do not
+    assert mrr.mrr_rank_buffer_pitch(128 * MiB, 8) == 128 * MiB + 5120
+    assert mrr.mrr_rank_buffer_pitch(384 * MiB - 100, 4) == 384 * MiB + 5120
+    assert mrr.mrr_rank_buffer_pitch(128 * MiB, 16) == 128 * MiB + 8192
+    assert mrr.mrr_rank_buffer_pitch(128 * MiB, 2) == 128 * MiB + 4096
+    assert mrr.mrr_rank_buffer_pitch(128 * MiB + 1, 8) == 128 * MiB + 4096 + 4096
+    assert mrr.mrr_rank_buffer_pitch(256 * MiB, 8) == 256 * MiB + 4096
+    assert mrr.mrr_rank_buffer_pitch(256 * MiB, 32) == 256 * MiB + 3072
     for n in (2, 4, 8, 16, 32):
-        for b in (4095, 4096, 4097, 12345, 256 * MiB):
+        for b in (4095, 4096, 4097, 12345, 128 * MiB, 256 * MiB, 384 * MiB):
             p = mrr.mrr_rank_buffer_pitch(b, n)
-            assert p % 16 == 0 and p >= b + 2048 and p < b + 8192
+            assert p % 1024 == 0 and p >= b + 2048 and p <= b + 8192
 
 
 def test_allreduce_dispatch_checks(lib):
