@@ -33,9 +33,12 @@
  *     Every call is stream-ordered and asynchronous: it validates its
  *     arguments on the host, launches, and returns without synchronising.
  *     No call allocates or frees memory, so calls may be captured in a HIP
- *     graph.
- *   - The caller owns every buffer.  The library keeps no device state; it
- *     caches only per-device properties (CU count, occupancy).
+ *     graph (the allocation-free entry point after its first call on a
+ *     device, which sets up its workspace).
+ *   - The caller owns every buffer.  Apart from the workspace of the
+ *     allocation-free packet entry point (mrr_allreduce_packet_noalloc,
+ *     below), the library keeps no device state; it caches only per-device
+ *     properties (CU count, LDS size, occupancy).
  *   - Validation happens before any launch: on an error nothing is launched
  *     and the specific status is returned.  MRR_LOG=1 in the environment
  *     prints one stderr line per refused call (see mrr_reload_env).
