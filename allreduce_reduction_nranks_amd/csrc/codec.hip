@@ -65,7 +65,7 @@ template <int Dir> __device__ __forceinline__ void codec_elem(const void* in, vo
     reinterpret_cast<uint8_t*>(out)[i] = (uint8_t)f32_to_fp8(reinterpret_cast<const float*>(in)[i]);
 }
 
-constexpr int kCodecThreads = 256;
+constexpr int kCodecThreads = 64;  // one wave per workgroup, as the RS/AG kernels
 
 // Vector path: tiles of kCodecThreads * U units, grid-stride, then the tail.
 template <int Dir, int U>
@@ -110,15 +110,19 @@ __global__ void __launch_bounds__(kCodecThreads) codec_scalar_k(const void* in, 
     codec_elem<Dir>(in, out, i);
 }
 
-// Units in flight per lane and 256-lane workgroups per CU, per direction,
-// measured on MI355X over 268,435,456 elements (U in {1,2,4,8} x {2..8}
-// workgroups per CU, one workgroup per tile): both decodes U=4 at 4 per CU
-// (fractions of the HBM peak: f16 0.79, f32 0.82), the f16 encode U=4 at 6
-// per CU (0.81) and the f32 encode U=2 at 6 per CU (0.81-0.83).
+// Units in flight per lane and single-wave workgroups per CU, per direction,
+// measured on MI355X over 268,435,456 elements (U in {1,2,4,8} x 4-32
+// workgroups per CU, one workgroup per tile, two runs each), fractions of the
+// HBM peak: E4M3B15 -> f16 U=4 x24 (0.79), -> f32 U=4 x16 (0.82); f16 ->
+// E4M3B15 U=4 x24 (0.81), f32 -> E4M3B15 U=2 x32 (0.85).  256-lane
+// workgroups (U=4 at 4 per CU for the decodes, 6 for the encodes; U=2 for the
+// f32 encode) ran 0.77 / 0.82 / 0.80 / 0.79 in the same session.
 // MRR_CODEC_U / MRR_CODEC_WPC override.
 constexpr int codec_unroll(int dir) { return dir == kEncF32 ? 2 : 4; }
-constexpr int codec_wg_per_cu(int dir) { return dir == kDecF16 || dir == kDecF32 ? 4 : 6; }
-// At most 2^22 workgroups of 256 lanes (2^30 work-items); past that a workgroup
+constexpr int codec_wg_per_cu(int dir) {
+  return dir == kDecF32 ? 16 : dir == kEncF32 ? 32 : 24;
+}
+// At most 2^22 workgroups of 64 lanes (2^28 work-items); past that a workgroup
 // walks several tiles.
 constexpr uint64_t kCodecMaxGrid = 1u << 22;
 template <int Dir, int U>
