@@ -24,7 +24,9 @@
 //     store instruction covers 1 KiB of one buffer), issues the loads of a
 //     rank group together (non-temporal: the data is touched once),
 //     accumulates in rank order 0..N-1, narrows once and stores the result
-//     to all N outputs (the all-gather) with non-temporal 16-byte stores;
+//     to all N outputs (the all-gather) with non-temporal 16-byte stores,
+//     written through to HBM at device scope where that measured faster
+//     (rsag_dev_stores);
 //   - few waves per CU stream best (two to twelve single-wave workgroups
 //     per CU, see the launch-shape table below): more loads in flight thrash
 //     DRAM rows across the 2N same-offset buffers, fewer leave HBM latency
@@ -45,18 +47,53 @@ namespace mrr {
 
 constexpr int kRsagThreads = 64;  // one wave per workgroup (all kernels but one shape below)
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Fourth word of a raw buffer descriptor on gfx9-family GPUs: 32-bit data
+// format, no swizzle, no index stride.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+
+// Streaming store at device scope (sc1 nt): written through to memory rather
+// than held in the XCD's L2 until evicted.  Issued as a buffer store whose
+// descriptor starts at the unit of the wave's first active lane and spans 64
+// units, so the active lanes must hold consecutive units from that lane on
+// (lane-contiguous tiles, or a prefix of one); a store outside the span is
+// dropped by the range check, never written elsewhere.  B = 16 or 8 bytes.
+template <int B, typename V>
+__device__ __forceinline__ void st_stream_dev(void* base, uint64_t unit, V v) {
+  static_assert(B == 16 || B == 8, "16- or 8-byte units");
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)unit);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(unit >> 32));
+  const uint64_t first = ((uint64_t)hi << 32) | lo;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<char*>(base) + first * B, (short)0, 64 * B, kBufferWord3);
+  constexpr int kDevNt = 18;  // cache policy: sc1 (device scope) | nt
+  if constexpr (B == 16)
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (uint32_t)(unit - first) * 16u, 0, kDevNt);
+  else
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (uint32_t)(unit - first) * 8u, 0, kDevNt);
+}
+// Streaming 16-byte store, device scope or not.
+template <bool kDev>
+__device__ __forceinline__ void st_out(void* base, uint64_t vec, u32x4 v) {
+  if constexpr (kDev) st_stream_dev<16>(base, vec, v);
+  else st_stream(base, vec, v);
+}
+
 // Launch shape, from sweeps of (units per lane U) x (workgroups per CU) of
 // this kernel on MI355X at 64 MiB and 256 MiB per rank (16- and 32-bit
 // inputs) and 32 MiB per rank (FP8 inputs at 8 ranks).  Streaming bandwidth is
 // bumpy in both knobs -- the 2N same-offset streams interact with the DRAM
 // channel and bank mapping -- so each entry is the setting that stayed near
 // the best across buffer sizes rather than a formula.
-//   16-bit and 32-bit inputs: N=2 U=2 x12, N=4 U=1 x8, N=8 U=1 x8,
+//   16-bit and 32-bit inputs: N=2 U=2 x12, N=4 U=1 x8, N=8 U=1 x8 (x6 for
+//                             f32 data: 0.82 against 0.78 at x8),
 //                             N=16 U=1 x4, N=32 U=1 x4 with loads in groups of
 //                             8 ranks (fractions of the HBM peak at 64 / 256 MiB
-//                             per rank: N=2 0.81 / 0.82, N=4 0.82 / 0.80,
-//                             N=8 0.81 (f16) / 0.77, N=16 0.78 / 0.76,
-//                             N=32 0.75 / 0.77; with groups of 16 ranks at 8
+//                             per rank, with the store policy of
+//                             rsag_dev_stores: N=2 0.81 / 0.83, N=4 0.83 / 0.81,
+//                             N=8 0.82 (f16) / 0.78, N=16 0.79 / 0.76-0.77,
+//                             N=32 0.74 / 0.78; with groups of 16 ranks at 8
 //                             per CU, N=32 ran 0.70 / 0.70)
 //   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: U=1 for FP8 and f16 outputs,
 //                             U=2 (128-lane tiles, below) x2 for f32 outputs,
@@ -64,15 +101,16 @@ constexpr int kRsagThreads = 64;  // one wave per workgroup (all kernels but one
 //                             rsag_wide_f32_kernel instead (rsag_wide_wg_per_cu);
 //                             N=2: U=4 times 2 for f16 and 4 for f32 outputs
 //                             (a lane loads 16 bytes per rank).  Workgroups per
-//                             CU, swept 4-16 at 32 MiB per rank (fractions of
-//                             the HBM peak at the chosen cap, E4M3B15 /
-//                             E4M3FN):
-//                               FP8 out: N=2 x16 (0.74 / 0.73), N=4 x12 / x8
-//                                 (0.75 / 0.77), N=8 x6 (0.81 / 0.78),
-//                                 N=16 x6 (0.76 / 0.77), N=32 x4 (0.74 / 0.73);
-//                               f16 out: N=2 x4 (0.74 / 0.75), N=4 x16 / x8
-//                                 (0.74 / 0.77), N=8 x6 (0.80 / 0.80),
-//                                 N=16 x4 (0.74 / 0.75), N=32 x6 (0.71 / 0.71).
+//                             CU, swept 4-16 at 32 MiB per rank with the store
+//                             policy of rsag_dev_stores (fractions of the HBM
+//                             peak at the chosen cap, E4M3B15 / E4M3FN, two
+//                             sessions):
+//                               FP8 out: N=2 x10 (0.78 / 0.76), N=4 x12 / x10
+//                                 (0.77 / 0.79), N=8 x6 (0.82 / 0.82),
+//                                 N=16 x4 (0.77 / 0.80), N=32 x4 (0.75 / 0.74);
+//                               f16 out: N=2 x8 / x4 (0.79 / 0.76), N=4 x16 / x10
+//                                 (0.76 / 0.81), N=8 x6 (0.82 / 0.82),
+//                                 N=16 x4 (0.75 / 0.77), N=32 x6 / x4 (0.71 / 0.73).
 //                             At 4 ranks fewer than 8 workgroups per CU starve
 //                             the memory system (E4M3B15 -> f16 0.39 at 4,
 //                             0.59 at 8).
@@ -99,14 +137,38 @@ constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
     const bool f16 = tout == kF16;
     if (tout == kF32) return n == 2 && !fn ? 8 : 2;  // 128-lane workgroups above 2 ranks
     switch (n) {
-      case 2: return f16 ? 4 : 16;
-      case 4: return fn ? 8 : f16 ? 16 : 12;
-      case 16: return f16 ? 4 : 6;
-      case 32: return f16 ? 6 : 4;
+      case 2: return f16 ? (fn ? 4 : 8) : 10;
+      case 4: return fn ? 10 : f16 ? 16 : 12;
+      case 16: return 4;
+      case 32: return f16 && !fn ? 6 : 4;
       default: return 6;
     }
   }
+  if (tin == kF32 && n == 8) return 6;
   return n == 2 ? 12 : n == 4 ? 8 : n == 8 ? 8 : 4;
+}
+// Output stores at device scope (sc1 nt, st_stream_dev) or plain streaming
+// (nt).  Device-scope stores are written through to HBM instead of waiting in
+// the XCD's L2 for eviction.  Measured on MI355X (two sessions, each kernel at
+// its best cap under either policy, fractions of the HBM peak, nt -> sc1 nt):
+//   16-bit data: N=2 0.81 -> 0.78 at 64 MiB per rank (kept nt), N=4 0.81-0.82
+//     -> 0.81-0.84, N=8 0.815-0.825 -> 0.811-0.825 (f16 a tie, bf16 1 % down:
+//     kept nt), N=16 0.74-0.78 -> 0.76-0.79, N=32 0.73-0.78 -> 0.74-0.78;
+//   f32 data (64 / 256 MiB per rank): N=2 0.80 / 0.83 -> 0.78 / 0.84 (kept
+//     nt), N=4 0.83 / 0.82 -> 0.83 / 0.83, N=8 0.82 / 0.78 -> 0.82 / 0.80
+//     (kept nt), N=16 0.77 / 0.77 -> 0.79 / 0.81,
+//     N=32 0.73 / 0.77 -> 0.74 / 0.78;
+//   FP8 data (E4M3B15 / E4M3FN, 32 MiB per rank) to FP8 or f16: +2 to +4 % at
+//     N=2 (E4M3FN -> f16 a tie), -1 to -3 % at N=4 (kept nt), +0 to +3 % at
+//     N=8, +1 to +3 % at 16 and +0 to +3 % at 32 ranks;
+//   FP8 to f32 (128-lane tiles at N=8): 0.72-0.73 -> 0.77 at N=8; E4M3FN at
+//     N=2 (64-lane, 16 codes per lane) 0.765 -> 0.741 (kept nt).
+// The wide FP8 -> f32 kernel and the one-pass FP8 -> f16 + FP8 kernel always
+// store at device scope (see them below).
+constexpr bool rsag_dev_stores(int n, int tin, int tout) {
+  if (!is_fp8(tin)) return n == 4 || n >= 16;
+  if (tout == kF32) return n != 2;
+  return n != 4;
 }
 // FP8 -> f32: workgroups per CU of rsag_wide_f32_kernel (16-value units,
 // stores through LDS), or 0 where the general kernel above stays faster.
@@ -117,10 +179,14 @@ constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
 //   E4M3FN:  N=2 0.76 -> 0.75 (kept general), N=4 0.62 -> 0.73 (x6), N=8 0.74 -> 0.71
 //            (kept general), N=16 0.69 -> 0.71 (x2), N=32 0.65 -> 0.67 (x2).
 // With the one-branch exponent-15 check the general kernel at 8 ranks runs
-// 0.74 for both formats at 2 per CU, against 0.71 for this one.
+// 0.74 for both formats at 2 per CU, against 0.71 for this one.  Its stores
+// are at device scope: E4M3B15 N=2 0.75 -> 0.78 (x12), N=4 0.75 -> 0.76 (x8
+// instead of x6), N=16 0.59-0.67 -> 0.71-0.73, N=32 0.65 -> 0.68.
 constexpr int rsag_wide_wg_per_cu(int n, int tin) {
-  return n == 2 ? (tin == kFP8 ? 12 : 0) : n == 4 ? 6 : (n == 16 || n == 32) ? 2 : 0;
+  return n == 2 ? (tin == kFP8 ? 12 : 0) : n == 4 ? 8 : (n == 16 || n == 32) ? 2 : 0;
 }
+// One-pass FP8 -> f16 + FP8: device-scope stores for both outputs (8 x 32 MiB
+// E4M3B15 0.751 -> 0.759, E4M3FN 0.757 -> 0.772, 2 x 32 MiB 0.722 -> 0.742).
 constexpr int rsag_dual_unroll(int n) { return n == 2 ? 8 : 2; }
 constexpr int rsag_dual_wg_per_cu(int) { return 4; }
 // Ranks whose vectors are loaded together before they are added: all of them
@@ -249,6 +315,7 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
   // 1385-1387 us in output order; at 8 and 32 ranks the rotation was 0.5-1 %
   // slower, so they keep output order, as do FP8 inputs (not measured).
   constexpr bool kRotate = N == 16 && !is_fp8(In);
+  constexpr bool kDev = Out2 != 0 || rsag_dev_stores(N, In, Out);
   const int k0 = kRotate ? (int)(blockIdx.x & (N - 1)) : 0;
 #pragma unroll
   for (int u = 0; u < UU; ++u) {
@@ -258,15 +325,18 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
     else o = encode16<Out>(acc[u]);
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      if constexpr (kRotate) st_stream(a.out[(k + k0) & (N - 1)], v, o);
-      else st_stream(a.out[k], v, o);
+      if constexpr (kRotate) st_out<kDev>(a.out[(k + k0) & (N - 1)], v, o);
+      else st_out<kDev>(a.out[k], v, o);
     }
     if constexpr (Out2 != 0) {
       static_assert(UE == 8, "second FP8 output needs 8-element units");
       uint32_t w2[2];
       encode8_fp8<Out2>(acc[u], special[u], w2);
+      u32x2 o2;
+      o2[0] = w2[0];
+      o2[1] = w2[1];
 #pragma unroll
-      for (int k = 0; k < N; ++k) st_words<2>(out2[k], v, w2);
+      for (int k = 0; k < N; ++k) st_stream_dev<8>(out2[k], v, o2);
     }
   }
 }
@@ -381,7 +451,7 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_wide_f32_kernel(const RsagA
       const u32x4 o = tr[j * kRsagThreads + lane];
       if (w < w_hi) {
 #pragma unroll
-        for (int k = 0; k < N; ++k) st_stream(a.out[k], w, o);
+        for (int k = 0; k < N; ++k) st_stream_dev<16>(a.out[k], w, o);
       }
     }
     __syncthreads();  // the next tile rewrites tr
@@ -405,6 +475,10 @@ constexpr int kAnyGroupWideMaxRanks = 20;
 
 template <int In, int Acc, int Out, int UU, int G>
 __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint64_t v0) {
+  // Device-scope output stores for 16- and 32-bit data (12 x 64 MiB f16
+  // 0.772 -> 0.780 of the HBM peak, 24 x 64 MiB bf16 0.753 -> 0.757); FP8
+  // data keeps plain streaming stores (6 x 32 MiB 0.799 against 0.792).
+  constexpr bool kDev = !is_fp8(In);
   constexpr int UE = Unit<In, Out>::UE;
   constexpr int D = Unit<In, Out>::D;
   constexpr int EPW = Unit<In, Out>::EPW;
@@ -471,14 +545,14 @@ __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint6
         void* const p1 = a.out[k + 1];
         void* const p2 = a.out[k + 2];
         void* const p3 = a.out[k + 3];
-        st_stream(p0, v, o);
-        st_stream(p1, v, o);
-        st_stream(p2, v, o);
-        st_stream(p3, v, o);
+        st_out<kDev>(p0, v, o);
+        st_out<kDev>(p1, v, o);
+        st_out<kDev>(p2, v, o);
+        st_out<kDev>(p3, v, o);
       }
-      for (; k < n; ++k) st_stream(a.out[k], v, o);
+      for (; k < n; ++k) st_out<kDev>(a.out[k], v, o);
     } else {
-      for (int k = 0; k < n; ++k) st_stream(a.out[k], v, o);
+      for (int k = 0; k < n; ++k) st_out<kDev>(a.out[k], v, o);
     }
   }
 }
