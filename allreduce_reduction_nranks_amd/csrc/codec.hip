@@ -113,14 +113,18 @@ __global__ void __launch_bounds__(kCodecThreads) codec_scalar_k(const void* in, 
 // Units in flight per lane and single-wave workgroups per CU, per direction,
 // measured on MI355X over 268,435,456 elements (U in {1,2,4,8} x 4-32
 // workgroups per CU, one workgroup per tile, two runs each), fractions of the
-// HBM peak: E4M3B15 -> f16 U=4 x24 (0.79), -> f32 U=4 x16 (0.82); f16 ->
-// E4M3B15 U=4 x24 (0.81), f32 -> E4M3B15 U=2 x32 (0.85).  256-lane
+// HBM peak: E4M3B15 -> f16 U=4 x16 (0.81), -> f32 U=4 x16 (0.82); f16 ->
+// E4M3B15 U=4 x24 (0.81), f32 -> E4M3B15 U=2 x24 (0.85).  A second session
+// moved two caps (E4M3B15 -> f16 x24 -> x16: 0.807 -> 0.813; f32 -> E4M3B15
+// x32 -> x24: 0.842 -> 0.853, mean of two A/B runs each).  256-lane
 // workgroups (U=4 at 4 per CU for the decodes, 6 for the encodes; U=2 for the
-// f32 encode) ran 0.77 / 0.82 / 0.80 / 0.79 in the same session.
+// f32 encode) ran 0.77 / 0.82 / 0.80 / 0.79 in the first session.  Stores at
+// device scope (written through the L2, as some RS/AG shapes use) were 0.5-1 %
+// slower in every direction, so the codec keeps plain streaming stores.
 // MRR_CODEC_U / MRR_CODEC_WPC override.
 constexpr int codec_unroll(int dir) { return dir == kEncF32 ? 2 : 4; }
 constexpr int codec_wg_per_cu(int dir) {
-  return dir == kDecF32 ? 16 : dir == kEncF32 ? 32 : 24;
+  return dir == kDecF32 || dir == kDecF16 ? 16 : 24;
 }
 // At most 2^22 workgroups of 64 lanes (2^28 work-items); past that a workgroup
 // walks several tiles.
