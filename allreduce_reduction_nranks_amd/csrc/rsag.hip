@@ -473,12 +473,10 @@ constexpr int kAnyGroup = 8;
 constexpr int kAnyGroupWide = 16;
 constexpr int kAnyGroupWideMaxRanks = 20;
 
-template <int In, int Acc, int Out, int UU, int G>
+// kDev: device-scope output stores (st_stream_dev); the launcher picks them
+// per rank count (rsag_any_dev_stores).
+template <int In, int Acc, int Out, int UU, int G, bool kDev>
 __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint64_t v0) {
-  // Device-scope output stores for 16- and 32-bit data (12 x 64 MiB f16
-  // 0.772 -> 0.780 of the HBM peak, 24 x 64 MiB bf16 0.753 -> 0.757); FP8
-  // data keeps plain streaming stores (6 x 32 MiB 0.799 against 0.792).
-  constexpr bool kDev = !is_fp8(In);
   constexpr int UE = Unit<In, Out>::UE;
   constexpr int D = Unit<In, Out>::D;
   constexpr int EPW = Unit<In, Out>::EPW;
@@ -557,7 +555,7 @@ __device__ __forceinline__ void reduce_store_any(const RsagArgs& a, int n, uint6
   }
 }
 
-template <int In, int Acc, int Out, int U, int G>
+template <int In, int Acc, int Out, int U, int G, bool kDev>
 __global__ void __launch_bounds__(kRsagThreads) rsag_any_kernel(const RsagArgs a) {
   const int n = (int)a.nranks;
   for (uint32_t i = blockIdx.x; i < a.launch_tiles; i += gridDim.x) {
@@ -567,12 +565,12 @@ __global__ void __launch_bounds__(kRsagThreads) rsag_any_kernel(const RsagArgs a
     const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
     const uint64_t v0 = v_lo + (uint64_t)tile * (kRsagThreads * U) + threadIdx.x;
     if (v0 + (uint64_t)(U - 1) * kRsagThreads < v_hi) {
-      reduce_store_any<In, Acc, Out, U, G>(a, n, v0);
+      reduce_store_any<In, Acc, Out, U, G, kDev>(a, n, v0);
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t v = v0 + (uint64_t)u * kRsagThreads;
-        if (v < v_hi) reduce_store_any<In, Acc, Out, 1, G>(a, n, v);
+        if (v < v_hi) reduce_store_any<In, Acc, Out, 1, G, kDev>(a, n, v);
       }
     }
   }
@@ -688,8 +686,29 @@ constexpr int rsag_any_unroll(int tin, int tout) {
 }
 static int rsag_any_multiplier(int) { return 1; }
 static int rsag_any_wg_per_cu(int n, int tin) {
-  if (is_fp8(tin)) return 8;
+  if (is_fp8(tin)) return n <= 4 ? 16 : 8;
   return n <= 4 ? 16 : n <= 8 ? 8 : 4;
+}
+// Output store scope of the runtime-N kernel, measured on MI355X at each
+// policy's best cap (two sessions; nt -> device scope): 16-bit data 3 x 64 MiB
+// 0.807 -> 0.800 (-2.6 % at the table's x16), 5 ranks a tie, 7 ranks +1.0 %,
+// 12 x 64 MiB f16 +1.0 %, 24 x 64 MiB bf16 +0.5 %; FP8 data 3 x 32 MiB -0.9 %
+// (E4M3FN -4.9 %), 5 ranks -0.5 %, 6 and 7 ranks +0.9 to +1.2 %.  So device
+// scope from 5 ranks of 16- and 32-bit data, plain stores for FP8 data.
+// (The FP8 cap at up to 4 ranks: 3 x 32 MiB E4M3B15 0.645 at x8 -> 0.780 at
+// x16, E4M3FN 0.659 -> 0.773.)
+constexpr int kAnyNtMaxRanks = 4;
+static bool rsag_any_dev_stores(int n, int tin) { return !is_fp8(tin) && n > kAnyNtMaxRanks; }
+// Groups of 8 ranks, M = mult units per lane.
+template <int In, int Acc, int Out, int U, bool kDev>
+static void launch_any_g8(int mult, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                          const RsagArgs& a) {
+  if (mult == 4)
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 4 * U, kAnyGroup, kDev>), grid, block, lds, s, a);
+  else if (mult == 2)
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 2 * U, kAnyGroup, kDev>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup, kDev>), grid, block, lds, s, a);
 }
 template <int In, int Acc, int Out>
 static void launch_any_typed(int n, int mult, const RsagShape& sh, const RsagArgs& a,
@@ -701,18 +720,19 @@ static void launch_any_typed(int n, int mult, const RsagShape& sh, const RsagArg
   // FP8 data or accumulators keep groups of 8 (as the compiled kernels do):
   // their per-rank decode state for 16 ranks no longer stays in registers.
   constexpr bool wide_ok = !is_fp8(In) && !is_fp8(Acc);
-  if (wide_ok && n > kAnyGroup && n <= kAnyGroupWideMaxRanks) {
-    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, wide_ok ? kAnyGroupWide : kAnyGroup>), grid,
-                       block, lds, s, a);
-  } else if constexpr (is_fp8(In)) {
-    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, lds, s, a);
+  if constexpr (wide_ok) {
+    if (n > kAnyGroup && n <= kAnyGroupWideMaxRanks) {
+      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroupWide, true>), grid, block, lds,
+                         s, a);
+      return;
+    }
+  }
+  if constexpr (is_fp8(In)) {
+    hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup, false>), grid, block, lds, s, a);
+  } else if (rsag_any_dev_stores(n, In)) {
+    launch_any_g8<In, Acc, Out, U, true>(mult, grid, block, lds, s, a);
   } else {
-    if (mult == 4)
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 4 * U, kAnyGroup>), grid, block, lds, s, a);
-    else if (mult == 2)
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, 2 * U, kAnyGroup>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((rsag_any_kernel<In, Acc, Out, U, kAnyGroup>), grid, block, lds, s, a);
+    launch_any_g8<In, Acc, Out, U, false>(mult, grid, block, lds, s, a);
   }
 }
 
