@@ -95,7 +95,11 @@ __device__ __forceinline__ void st_out(void* base, uint64_t vec, u32x4 v) {
 //                             N=8 0.82 (f16) / 0.78, N=16 0.79 / 0.76-0.77,
 //                             N=32 0.74 / 0.78; with groups of 16 ranks at 8
 //                             per CU, N=32 ran 0.70 / 0.70)
-//   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: U=1 for FP8 and f16 outputs,
+//   FP8 inputs (E4M3B15 and OCP E4M3FN), N>2: U=1 for FP8 and f16 outputs
+//                             (U=2 for E4M3B15 at N=4: at its best cap, x6,
+//                             0.77-0.78 / 0.77 to FP8 / f16 against 0.77 /
+//                             0.76 for U=1 at x12 / x16; E4M3FN loses 4-5 %
+//                             with U=2),
 //                             U=2 (128-lane tiles, below) x2 for f32 outputs,
 //                             which at most rank counts take
 //                             rsag_wide_f32_kernel instead (rsag_wide_wg_per_cu);
@@ -105,11 +109,11 @@ __device__ __forceinline__ void st_out(void* base, uint64_t vec, u32x4 v) {
 //                             policy of rsag_dev_stores (fractions of the HBM
 //                             peak at the chosen cap, E4M3B15 / E4M3FN, two
 //                             sessions):
-//                               FP8 out: N=2 x10 (0.78 / 0.76), N=4 x12 / x10
+//                               FP8 out: N=2 x10 (0.78 / 0.76), N=4 x6 (U=2) / x10
 //                                 (0.77 / 0.79), N=8 x6 (0.82 / 0.82),
 //                                 N=16 x4 (0.77 / 0.80), N=32 x4 (0.75 / 0.74);
-//                               f16 out: N=2 x8 / x4 (0.79 / 0.76), N=4 x16 / x10
-//                                 (0.76 / 0.81), N=8 x6 (0.82 / 0.82),
+//                               f16 out: N=2 x8 / x4 (0.79 / 0.76), N=4 x6 (U=2) / x10
+//                                 (0.77 / 0.81), N=8 x6 (0.82 / 0.82),
 //                                 N=16 x4 (0.75 / 0.77), N=32 x6 / x4 (0.71 / 0.73).
 //                             At 4 ranks fewer than 8 workgroups per CU starve
 //                             the memory system (E4M3B15 -> f16 0.39 at 4,
@@ -127,6 +131,7 @@ constexpr int rsag_threads(int n, int tin, int tout) {
 constexpr int rsag_unroll(int n, int tin, int tout) {
   if (is_fp8(tin)) {
     if (n == 2) return 4 * (tout == kF32 ? 4 : tout == kF16 ? 2 : 1);
+    if (n == 4 && tin == kFP8 && tout != kF32) return 2;
     return tout == kF32 ? 2 : 1;
   }
   return n == 2 ? 2 : 1;
@@ -138,7 +143,7 @@ constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
     if (tout == kF32) return n == 2 && !fn ? 8 : 2;  // 128-lane workgroups above 2 ranks
     switch (n) {
       case 2: return f16 ? (fn ? 4 : 8) : 10;
-      case 4: return fn ? 10 : f16 ? 16 : 12;
+      case 4: return fn ? 10 : 6;  // E4M3B15: two units per lane
       case 16: return 4;
       case 32: return f16 && !fn ? 6 : 4;
       default: return 6;
