@@ -120,7 +120,12 @@ __device__ __forceinline__ void st_out(void* base, uint64_t vec, u32x4 v) {
 //                                 N=16 x4 (0.77 / 0.80), N=32 x4 (0.75 / 0.74);
 //                               f16 out: N=2 x8 / x4 (0.79 / 0.76), N=4 x6 (U=2) / x10
 //                                 (0.77 / 0.81), N=8 x6 (0.82 / 0.82),
-//                                 N=16 x4 (0.75 / 0.77), N=32 x6 / x4 (0.71 / 0.73).
+//                                 N=16 x4 (0.75 / 0.77), N=32 x6 (0.71 / 0.71).
+//                             A paired sweep (every cap timed in turn on the
+//                             same buffers, three processes) put this table
+//                             within 0.6 % of the best cap at every FP8 shape
+//                             and 16-bit shape at 2-32 ranks, after moving
+//                             E4M3FN -> f16 at 32 ranks from x4 to x6 (+1.4 %).
 //                             At 4 ranks fewer than 8 workgroups per CU starve
 //                             the memory system (E4M3B15 -> f16 0.39 at 4,
 //                             0.59 at 8).
@@ -151,7 +156,7 @@ constexpr int rsag_wg_per_cu(int n, int tin, int tout) {
       case 2: return f16 ? (fn ? 4 : 8) : 10;
       case 4: return fn ? 10 : 6;  // E4M3B15: two units per lane
       case 16: return 4;
-      case 32: return f16 && !fn ? 6 : 4;
+      case 32: return f16 ? 6 : 4;
       default: return 6;
     }
   }
