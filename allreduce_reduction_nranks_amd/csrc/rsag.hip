@@ -86,14 +86,13 @@ __device__ __forceinline__ void st_out(void* base, uint64_t vec, u32x4 v) {
 // bumpy in both knobs -- the 2N same-offset streams interact with the DRAM
 // channel and bank mapping -- so each entry is the setting that stayed near
 // the best across buffer sizes rather than a formula.
-//   16-bit and 32-bit inputs: N=2 U=2 x12, N=4 U=1 x8, N=8 U=1 x6 (x8 until
-//                             a paired comparison -- both caps timed in
-//                             turn on the same buffers in one process, four
-//                             processes -- gave x6 faster at 16 / 32 / 96 /
-//                             128 / 256 MiB per rank by 1.5 / 3.0 / 1.3 / 0.2
-//                             / 0.7 %, 0.15 % slower at 64 MiB f16, 0.2 %
-//                             faster at 64 MiB bf16 and 0.3 % slower at
-//                             512 MiB; f32 data 0.82 against 0.78),
+//   16-bit and 32-bit inputs: N=2 U=2 x12, N=4 U=1 x8, N=8 U=1 x6 (x8
+//                             before; three alternating runs of the
+//                             benchmark each, one session: 8 x 64 MiB f16
+//                             164.6 against 164.9 us, 8 x 32 MiB f16 84.6
+//                             against 88.7 us, 8 x 256 MiB bf16 691.4
+//                             against 687.5 us; f32 data 0.82 against
+//                             0.78),
 //                             N=16 U=1 x4, N=32 U=1 x4 with loads in groups of
 //                             8 ranks (fractions of the HBM peak at 64 / 256 MiB
 //                             per rank, with the store policy of
