@@ -65,6 +65,8 @@ def table_unroll(n, t, tout):
     if t in ("fp8", "fp8fn"):
         if n == 2:
             return 4 * {"f32": 4, "f16": 2}.get(tout, 1)
+        if n == 4 and t == "fp8" and tout != "f32":
+            return 2
         return 2 if tout == "f32" else 1
     return 2 if n == 2 else 1
 
@@ -209,6 +211,45 @@ def test_in_place(t):
     want = oracle.allreduce([bits(x) for x in ins], t, "f32", t)
     run(ins, t, "f32", t, outs=ins)
     check_all(ins, want, t, "in place")
+
+
+def views_at_offsets(t, n, count, fill, step):
+    # rank buffer r starts (r + 1) * step bytes into its own allocation:
+    # 16-byte aligned (the vector kernels run) but off the 256-byte grid
+    out = []
+    for r in range(n):
+        off = (r + 1) * step
+        raw = torch.empty(count * OUT_SIZE[t] + off + 64, dtype=torch.uint8, device="cuda")
+        raw.fill_(fill)
+        out.append(raw[off:off + count * OUT_SIZE[t]].view(TORCH[t]))
+    return out
+
+
+# Shapes whose output stores are device-scope buffer stores (4, 16 and 32
+# ranks of 16/32-bit data, FP8 to FP8 / f16 at 2, 8, 16 and 32 ranks, FP8 to
+# f32 in the 128-lane and the wide kernel) and two with plain streaming
+# stores (8 ranks of f16, 4 ranks of E4M3B15 at two units per lane).
+OFFSET_CASES = [(4, "bf16", "f32", "bf16"), (16, "f16", "f32", "f16"), (32, "bf16", "f32", "bf16"),
+                (16, "f32", "f32", "f32"), (2, "fp8", "f32", "fp8"), (8, "fp8fn", "f32", "f16"),
+                (8, "fp8", "f32", "f32"), (16, "fp8", "f32", "f32"), (4, "fp8fn", "f32", "f32"),
+                (32, "fp8", "f32", "f16"), (8, "f16", "f32", "f16"), (4, "fp8", "f32", "fp8")]
+
+
+@pytest.mark.parametrize("n,t,acc,tout", OFFSET_CASES, ids=["%d-%s-%s-%s" % c for c in OFFSET_CASES])
+@pytest.mark.parametrize("step", [16, 48])
+def test_vector_kernels_at_16_byte_offsets(n, t, acc, tout, step):
+    u = table_unroll(n, t, tout)
+    ue = 16 // OUT_SIZE[tout]
+    count = n * 64 * u * (3 * 512 // n + 1) * ue + 13
+    announce("rsag 16-byte offsets", n, t, acc, tout, step, count)
+    base = inputs_for(t, n, count, seed0=700 + n)
+    ins = views_at_offsets(t, n, count, 0, step)
+    for dst, src in zip(ins, base):
+        dst.copy_(src)
+    outs = views_at_offsets(tout, n, count, 0xA5, step + 16)
+    run(ins, t, acc, tout, outs=outs)
+    want = oracle.allreduce([bits(x) for x in base], t, acc, tout)
+    check_all(outs, want, tout, "offset %d n=%d %s/%s/%s" % (step, n, t, acc, tout))
 
 
 @pytest.mark.parametrize("t,off", [("f16", 1), ("bf16", 3), ("f32", 1), ("fp8", 5)])
