@@ -184,6 +184,18 @@ constexpr bool rsag_dev_stores(int n, int tin, int tout) {
   if (tout == kF32) return n != 2;
   return n != 4;
 }
+// 8 ranks of 16- or 32-bit data with at least 128 MiB of input per rank: a
+// second instance of the kernel stores at device scope, at 4 workgroups per
+// CU.  Measured on MI355X with three alternating runs of the benchmark per
+// setting in one session (us per call; plain stores at 6 per CU / device
+// scope at 6 / device scope at 4): 8 x 256 MiB bf16 689.7 / 693.0 / 683.3,
+// 8 x 128 MiB bf16 331.8 / 333.4 / 327.2, 8 x 64 MiB f16 165.3 / 166.5 /
+// 165.6 (so 64 MiB and below keep the plain stores).
+constexpr uint64_t kLargeDevBytes = (uint64_t)128 << 20;
+constexpr int kLargeDevWgPerCu = 4;
+constexpr bool rsag_large_dev(int n, int tin, uint64_t bytes_per_rank) {
+  return n == 8 && !is_fp8(tin) && bytes_per_rank >= kLargeDevBytes;
+}
 // FP8 -> f32: workgroups per CU of rsag_wide_f32_kernel (16-value units,
 // stores through LDS), or 0 where the general kernel above stays faster.
 // Measured on MI355X, 32 MiB of codes per rank, fractions of the HBM peak,
@@ -271,7 +283,10 @@ __device__ __forceinline__ void fp8_unit_exact(const void* const* in, int n, uin
 //
 // Out2 != 0 (FP8 types only, with Out = f16): each unit's 8 sums are also
 // encoded to Out2 and stored, 8 bytes per lane, to out2[0..N-1].
-template <int N, int In, int Acc, int Out, int UU, int G, int Out2 = 0, int T = kRsagThreads>
+// kLarge: the instance for large buffers at 8 ranks (rsag_large_dev), which
+// stores at device scope.
+template <int N, int In, int Acc, int Out, int UU, int G, int Out2 = 0, int T = kRsagThreads,
+          bool kLarge = false>
 __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
                                              void* const* out2 = nullptr) {
   constexpr int UE = Unit<In, Out>::UE;
@@ -329,7 +344,7 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
   // 1385-1387 us in output order; at 8 and 32 ranks the rotation was 0.5-1 %
   // slower, so they keep output order, as do FP8 inputs (not measured).
   constexpr bool kRotate = N == 16 && !is_fp8(In);
-  constexpr bool kDev = Out2 != 0 || rsag_dev_stores(N, In, Out);
+  constexpr bool kDev = Out2 != 0 || kLarge || rsag_dev_stores(N, In, Out);
   const int k0 = kRotate ? (int)(blockIdx.x & (N - 1)) : 0;
 #pragma unroll
   for (int u = 0; u < UU; ++u) {
@@ -356,7 +371,7 @@ __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
 }
 
 // The persistent tile loop shared by the single- and dual-output kernels.
-template <int N, int In, int Acc, int Out, int U, int Out2, int T = kRsagThreads>
+template <int N, int In, int Acc, int Out, int U, int Out2, int T = kRsagThreads, bool kLarge = false>
 __device__ __forceinline__ void rsag_vec_body(const RsagArgs& a, void* const* out2) {
   constexpr int G = rsag_group(N, In, Acc);
   for (uint32_t i = blockIdx.x; i < a.launch_tiles; i += gridDim.x) {
@@ -366,12 +381,12 @@ __device__ __forceinline__ void rsag_vec_body(const RsagArgs& a, void* const* ou
     const uint64_t v_hi = v_lo + a.chunk_vecs < a.total_vecs ? v_lo + a.chunk_vecs : a.total_vecs;
     const uint64_t v0 = v_lo + (uint64_t)tile * (T * U) + threadIdx.x;
     if (v0 + (uint64_t)(U - 1) * T < v_hi) {
-      reduce_store<N, In, Acc, Out, U, G, Out2, T>(a, v0, out2);
+      reduce_store<N, In, Acc, Out, U, G, Out2, T, kLarge>(a, v0, out2);
     } else {  // the last, partial tile of a chunk: unit by unit
 #pragma nounroll
       for (int u = 0; u < U; ++u) {
         const uint64_t v = v0 + (uint64_t)u * T;
-        if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G, Out2, T>(a, v, out2);
+        if (v < v_hi) reduce_store<N, In, Acc, Out, 1, G, Out2, T, kLarge>(a, v, out2);
       }
     }
   }
@@ -381,9 +396,9 @@ __device__ __forceinline__ void rsag_vec_body(const RsagArgs& a, void* const* ou
     reduce_elem<In, Acc, Out, Out2>(a.in, a.out, N, a.tail_begin + threadIdx.x, out2);
 }
 
-template <int N, int In, int Acc, int Out, int U, int T>
+template <int N, int In, int Acc, int Out, int U, int T, bool kLarge>
 __global__ void __launch_bounds__(T) rsag_vec_kernel(const RsagArgs a) {
-  rsag_vec_body<N, In, Acc, Out, U, 0, T>(a, nullptr);
+  rsag_vec_body<N, In, Acc, Out, U, 0, T, kLarge>(a, nullptr);
 }
 
 // FP8 inputs, f16 outputs plus the FP8 re-encode of the same sums.
@@ -669,16 +684,30 @@ static void launch_wide_typed(int nranks, const RsagShape& sh, const RsagArgs& a
 }
 
 template <int In, int Acc, int Out>
-static void launch_vec_typed(int nranks, const RsagShape& sh, const RsagArgs& a, hipStream_t s) {
+static void launch_vec_typed(int nranks, bool large, const RsagShape& sh, const RsagArgs& a,
+                             hipStream_t s) {
   switch (nranks) {
 #define MRR_CASE(N)                                                                          \
   case N:                                                                                    \
     hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In, Out),            \
-                                        rsag_threads(N, In, Out)>),                          \
+                                        rsag_threads(N, In, Out), false>),                   \
                        sh.grid, dim3(rsag_threads(N, In, Out)), sh.lds, s, a);               \
     break;
-    MRR_CASE(2) MRR_CASE(4) MRR_CASE(8) MRR_CASE(16) MRR_CASE(32)
+    MRR_CASE(2) MRR_CASE(4) MRR_CASE(16) MRR_CASE(32)
 #undef MRR_CASE
+    case 8:
+      if constexpr (!is_fp8(In)) {
+        if (large) {
+          hipLaunchKernelGGL((rsag_vec_kernel<8, In, Acc, Out, rsag_unroll(8, In, Out),
+                                              rsag_threads(8, In, Out), true>),
+                             sh.grid, dim3(rsag_threads(8, In, Out)), sh.lds, s, a);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((rsag_vec_kernel<8, In, Acc, Out, rsag_unroll(8, In, Out),
+                                          rsag_threads(8, In, Out), false>),
+                         sh.grid, dim3(rsag_threads(8, In, Out)), sh.lds, s, a);
+      break;
     default: break;
   }
 }
@@ -838,12 +867,16 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
       return hipGetLastError();
     }
     if (a.launch_tiles == 0 && a.tail_count == 0) return hipSuccess;
-    const RsagShape sh = rsag_shape(
-        small ? 8 : any_n ? rsag_any_wg_per_cu(n, In) : rsag_wg_per_cu(n, In, Out), a.launch_tiles);
+    const bool large = !any_n && rsag_large_dev(n, In, count * (uint64_t)Ty<In>::size);
+    const RsagShape sh = rsag_shape(small   ? 8
+                                    : any_n ? rsag_any_wg_per_cu(n, In)
+                                    : large ? kLargeDevWgPerCu
+                                            : rsag_wg_per_cu(n, In, Out),
+                                    a.launch_tiles);
     if (any_n)
       launch_any_typed<In, Acc, Out>(n, mult, sh, a, stream);
     else
-      launch_vec_typed<In, Acc, Out>(n, sh, a, stream);
+      launch_vec_typed<In, Acc, Out>(n, large, sh, a, stream);
   } else {
     RsagScalarArgs a = {};
     for (int r = 0; r < n; ++r) {

@@ -413,6 +413,39 @@ def test_rank_sweep_256mib_bf16_whole(n):
     torch.cuda.empty_cache()
 
 
+# 8 ranks with at least 128 MiB of input per rank run a second instance of
+# the compiled kernel (device-scope stores, 4 workgroups per CU).  Sizes just
+# above that threshold with a ragged tail, every element of every output, and
+# one rank's share written only into its chunk.
+LARGE8_CASES = [("f16", "f32", "f16", (64 << 20) + 4099), ("f32", "f32", "f32", (32 << 20) + 13),
+                ("bf16", "bf16", "bf16", (64 << 20) + 1)]
+
+
+@pytest.mark.parametrize("t,acc,tout,count", LARGE8_CASES, ids=["-".join(c[:3]) for c in LARGE8_CASES])
+def test_large_buffers_at_8_ranks(t, acc, tout, count):
+    n = 8
+    announce("rsag large 8 ranks", t, acc, tout, count)
+    ins = inputs_for(t, n, count, seed0=1200, device="cuda")
+    outs = [empty(tout, count, 0xA5) for _ in range(n)]
+    run(ins, t, acc, tout, outs=outs)
+    host = [bits(x) for x in ins]
+    want = oracle_allreduce_threaded(host, t, acc, tout)
+    assert_outputs_match(outs, want, tout, "8 ranks large %s/%s/%s" % (t, acc, tout))
+    # rank 5's share: its chunk equals the oracle, everything else keeps the fill
+    share = [empty(tout, count, 0x5A) for _ in range(n)]
+    run(ins, t, acc, tout, rank=5, outs=share)
+    per = -(-count // n)
+    chunk = -(-per // CHUNK_ALIGN[t]) * CHUNK_ALIGN[t]
+    lo, hi = min(count, 5 * chunk), min(count, 6 * chunk)
+    for k in range(n):
+        b = bits(share[k])
+        assert_bits_equal(b[lo:hi], want[lo:hi], tout, "rank 5 share out[%d]" % k)
+        untouched = np.concatenate([b[:lo], b[hi:]]).view(np.uint8)
+        assert np.all(untouched == 0x5A), "rank 5 wrote outside its chunk (out[%d])" % k
+    del ins, outs, share, host
+    torch.cuda.empty_cache()
+
+
 # Launches of more tiles than MRR_MAX_GRID workgroups: each workgroup walks
 # several tiles (the path calls above 2^24 tiles take), including partial
 # tiles at chunk ends and the element tail (the mrr_env fixture sets the override).
