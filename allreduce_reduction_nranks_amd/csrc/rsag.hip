@@ -184,18 +184,24 @@ constexpr bool rsag_dev_stores(int n, int tin, int tout) {
   if (tout == kF32) return n != 2;
   return n != 4;
 }
-// 8 ranks of 16- or 32-bit data with at least 128 MiB of input per rank: a
-// second instance of the kernel stores at device scope, at 4 workgroups per
-// CU.  Measured on MI355X with three alternating runs of the benchmark per
-// setting in one session (us per call; plain stores at 6 per CU / device
-// scope at 6 / device scope at 4): 8 x 256 MiB bf16 689.7 / 693.0 / 683.3,
-// 8 x 128 MiB bf16 331.8 / 333.4 / 327.2, 8 x 64 MiB f16 165.3 / 166.5 /
-// 165.6 (so 64 MiB and below keep the plain stores).
-constexpr uint64_t kLargeDevBytes = (uint64_t)128 << 20;
-constexpr int kLargeDevWgPerCu = 4;
+// Large buffers of 16- or 32-bit data at 8 ranks (from 128 MiB of input per
+// rank) and 2 ranks (from 256 MiB): a second instance of the kernel stores at
+// device scope, at 4 (8 ranks) or 8 (2 ranks) workgroups per CU.  Measured on
+// MI355X with three alternating runs of the benchmark per setting in one
+// session (us per call):
+//   8 ranks, plain stores at 6 per CU / device scope at 6 / device scope at
+//   4: 8 x 256 MiB bf16 689.7 / 693.0 / 683.3, 8 x 128 MiB 331.8 / 333.4 /
+//   327.2, 8 x 64 MiB f16 165.3 / 166.5 / 165.6;
+//   2 ranks, plain stores at 12 per CU / device scope at 12 / device scope
+//   at 8: 2 x 512 MiB bf16 333.0 / 326.4 / 324.2, 2 x 256 MiB 165.0 / 162.2
+//   / 161.8, 2 x 128 MiB 82.3 / 83.3 / 85.2.
 constexpr bool rsag_large_dev(int n, int tin, uint64_t bytes_per_rank) {
-  return n == 8 && !is_fp8(tin) && bytes_per_rank >= kLargeDevBytes;
+  if (is_fp8(tin)) return false;
+  if (n == 8) return bytes_per_rank >= ((uint64_t)128 << 20);
+  if (n == 2) return bytes_per_rank >= ((uint64_t)256 << 20);
+  return false;
 }
+constexpr int rsag_large_dev_wg_per_cu(int n) { return n == 8 ? 4 : 8; }
 // FP8 -> f32: workgroups per CU of rsag_wide_f32_kernel (16-value units,
 // stores through LDS), or 0 where the general kernel above stays faster.
 // Measured on MI355X, 32 MiB of codes per rank, fractions of the HBM peak,
@@ -283,8 +289,8 @@ __device__ __forceinline__ void fp8_unit_exact(const void* const* in, int n, uin
 //
 // Out2 != 0 (FP8 types only, with Out = f16): each unit's 8 sums are also
 // encoded to Out2 and stored, 8 bytes per lane, to out2[0..N-1].
-// kLarge: the instance for large buffers at 8 ranks (rsag_large_dev), which
-// stores at device scope.
+// kLarge: the instance for large buffers at 2 and 8 ranks (rsag_large_dev),
+// which stores at device scope.
 template <int N, int In, int Acc, int Out, int UU, int G, int Out2 = 0, int T = kRsagThreads,
           bool kLarge = false>
 __device__ __forceinline__ void reduce_store(const RsagArgs& a, uint64_t v0,
@@ -693,21 +699,25 @@ static void launch_vec_typed(int nranks, bool large, const RsagShape& sh, const 
                                         rsag_threads(N, In, Out), false>),                   \
                        sh.grid, dim3(rsag_threads(N, In, Out)), sh.lds, s, a);               \
     break;
-    MRR_CASE(2) MRR_CASE(4) MRR_CASE(16) MRR_CASE(32)
+    MRR_CASE(4) MRR_CASE(16) MRR_CASE(32)
 #undef MRR_CASE
-    case 8:
-      if constexpr (!is_fp8(In)) {
-        if (large) {
-          hipLaunchKernelGGL((rsag_vec_kernel<8, In, Acc, Out, rsag_unroll(8, In, Out),
-                                              rsag_threads(8, In, Out), true>),
-                             sh.grid, dim3(rsag_threads(8, In, Out)), sh.lds, s, a);
-          break;
-        }
-      }
-      hipLaunchKernelGGL((rsag_vec_kernel<8, In, Acc, Out, rsag_unroll(8, In, Out),
-                                          rsag_threads(8, In, Out), false>),
-                         sh.grid, dim3(rsag_threads(8, In, Out)), sh.lds, s, a);
-      break;
+// 2 and 8 ranks: a second instance for large buffers (rsag_large_dev).
+#define MRR_CASE_LARGE(N)                                                                    \
+  case N:                                                                                    \
+    if constexpr (!is_fp8(In)) {                                                             \
+      if (large) {                                                                           \
+        hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In, Out),        \
+                                            rsag_threads(N, In, Out), true>),                \
+                           sh.grid, dim3(rsag_threads(N, In, Out)), sh.lds, s, a);           \
+        break;                                                                               \
+      }                                                                                      \
+    }                                                                                        \
+    hipLaunchKernelGGL((rsag_vec_kernel<N, In, Acc, Out, rsag_unroll(N, In, Out),            \
+                                        rsag_threads(N, In, Out), false>),                   \
+                       sh.grid, dim3(rsag_threads(N, In, Out)), sh.lds, s, a);               \
+    break;
+    MRR_CASE_LARGE(2) MRR_CASE_LARGE(8)
+#undef MRR_CASE_LARGE
     default: break;
   }
 }
@@ -870,7 +880,7 @@ static hipError_t launch_rsag_typed(const RsagPlan& p, const void* const* inputs
     const bool large = !any_n && rsag_large_dev(n, In, count * (uint64_t)Ty<In>::size);
     const RsagShape sh = rsag_shape(small   ? 8
                                     : any_n ? rsag_any_wg_per_cu(n, In)
-                                    : large ? kLargeDevWgPerCu
+                                    : large ? rsag_large_dev_wg_per_cu(n)
                                             : rsag_wg_per_cu(n, In, Out),
                                     a.launch_tiles);
     if (any_n)

@@ -413,35 +413,37 @@ def test_rank_sweep_256mib_bf16_whole(n):
     torch.cuda.empty_cache()
 
 
-# 8 ranks with at least 128 MiB of input per rank run a second instance of
-# the compiled kernel (device-scope stores, 4 workgroups per CU).  Sizes just
-# above that threshold with a ragged tail, every element of every output, and
-# one rank's share written only into its chunk.
-LARGE8_CASES = [("f16", "f32", "f16", (64 << 20) + 4099), ("f32", "f32", "f32", (32 << 20) + 13),
-                ("bf16", "bf16", "bf16", (64 << 20) + 1)]
+# 8 ranks with at least 128 MiB of input per rank, and 2 ranks with at least
+# 256 MiB, run a second instance of the compiled kernel (device-scope
+# stores, fewer workgroups per CU).  Sizes just above those thresholds with
+# a ragged tail, every element of every output, and one rank's share
+# written only into its chunk.
+LARGE_CASES = [(8, "f16", "f32", "f16", (64 << 20) + 4099), (8, "f32", "f32", "f32", (32 << 20) + 13),
+               (8, "bf16", "bf16", "bf16", (64 << 20) + 1), (2, "f16", "f32", "f16", (128 << 20) + 4099),
+               (2, "f32", "f32", "f32", (64 << 20) + 13)]
 
 
-@pytest.mark.parametrize("t,acc,tout,count", LARGE8_CASES, ids=["-".join(c[:3]) for c in LARGE8_CASES])
-def test_large_buffers_at_8_ranks(t, acc, tout, count):
-    n = 8
-    announce("rsag large 8 ranks", t, acc, tout, count)
-    ins = inputs_for(t, n, count, seed0=1200, device="cuda")
+@pytest.mark.parametrize("n,t,acc,tout,count", LARGE_CASES, ids=["%d-%s-%s-%s" % c[:4] for c in LARGE_CASES])
+def test_large_buffer_instances(n, t, acc, tout, count):
+    announce("rsag large buffers", n, t, acc, tout, count)
+    ins = inputs_for(t, n, count, seed0=1200 + n, device="cuda")
     outs = [empty(tout, count, 0xA5) for _ in range(n)]
     run(ins, t, acc, tout, outs=outs)
     host = [bits(x) for x in ins]
     want = oracle_allreduce_threaded(host, t, acc, tout)
-    assert_outputs_match(outs, want, tout, "8 ranks large %s/%s/%s" % (t, acc, tout))
-    # rank 5's share: its chunk equals the oracle, everything else keeps the fill
+    assert_outputs_match(outs, want, tout, "%d ranks large %s/%s/%s" % (n, t, acc, tout))
+    # one rank's share: its chunk equals the oracle, everything else keeps the fill
+    r = min(5, n - 1)
     share = [empty(tout, count, 0x5A) for _ in range(n)]
-    run(ins, t, acc, tout, rank=5, outs=share)
+    run(ins, t, acc, tout, rank=r, outs=share)
     per = -(-count // n)
     chunk = -(-per // CHUNK_ALIGN[t]) * CHUNK_ALIGN[t]
-    lo, hi = min(count, 5 * chunk), min(count, 6 * chunk)
+    lo, hi = min(count, r * chunk), min(count, (r + 1) * chunk)
     for k in range(n):
         b = bits(share[k])
-        assert_bits_equal(b[lo:hi], want[lo:hi], tout, "rank 5 share out[%d]" % k)
+        assert_bits_equal(b[lo:hi], want[lo:hi], tout, "rank %d share out[%d]" % (r, k))
         untouched = np.concatenate([b[:lo], b[hi:]]).view(np.uint8)
-        assert np.all(untouched == 0x5A), "rank 5 wrote outside its chunk (out[%d])" % k
+        assert np.all(untouched == 0x5A), "rank %d wrote outside its chunk (out[%d])" % (r, k)
     del ins, outs, share, host
     torch.cuda.empty_cache()
 
